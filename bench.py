@@ -1,0 +1,302 @@
+"""Benchmark of the ZeRO++ quantized-communication hot path on one MI355X.
+
+One step is one rank's pass through every kernel of the path, at full size:
+  qwZ  (GPT layer at hidden 8192, fp16, block 256, 16 ranks)
+    K1 zpq_quant_i8             quantize this rank's 1/16 weight shard
+    K2 zpq_dequant_i8           dequantize the gathered buffer (16 shards)
+  qgZ  (138B-model layer gradient: FFN 12288x49152 + QKV 12288x36864, fp16,
+        INT4 block 64, L = 8 local ranks, N = 48 nodes)
+    K3 zpq_qgz_reorder_quant_i4             slice reorder + INT4 quantize
+    K4 zpq_qgz_dequant_reduce_requant_i4    hop 1: 8 received chunks -> INT4
+    K5 zpq_qgz_dequant_reduce_requant_i4    hop 2: 48 received chunks -> fp16 average
+The all-gather and all-to-alls are simulated: the receive buffers are filled
+once before timing (gathered buffer = the 16 shards' quantization; hop-1
+receive = this rank's own 8 send chunks; hop-2 receive = the 48 send positions
+of its own hop-1 result), so each kernel reads a buffer the previous kernel
+did not just write and nothing is served from the 256 MB MALL.
+
+Prints one JSON line.  `value` is the step's effective HBM bandwidth:
+algorithmic bytes of all five kernels / wall time per step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective HBM GB/s per kernel and % of MI355X peak (qwZ quant/dequant, qgZ hop)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--cpu-fraction", type=float, default=1.0 / 16)
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="per-kernel HBM bytes from rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(collectives are simulated in one GPU's memory); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_quantized_communication_amd as zpq
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    T = torch
+
+    # ---------------- workloads ----------------
+    qw = synth.QWZ_LAYER
+    Bw, Ww, nw = qw["block"], qw["world"], qw["n"]
+    Sw = nw // Ww
+    qg = synth.QGZ_FUSED
+    L, N, Bg, ng = qg["L"], qg["N"], qg["block"], qg["n"]
+    W = L * N
+    Sg = ng // W
+    chunk = ng // L
+
+    t0 = time.time()
+    print(f"[bench] generating qwZ layer ({nw} fp16)", file=sys.stderr, flush=True)
+    layer_h = synth.qwz_layer()
+    layer = torch.from_numpy(layer_h).to(dev)
+    print(f"[bench] generating qgZ gradient ({ng} fp16)", file=sys.stderr, flush=True)
+    grad_h = synth.qgz_fused()
+    grad = torch.from_numpy(grad_h).to(dev)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    shard = layer[:Sw]
+    e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
+    shard_codes, shard_scales = e(Sw, T.int8), e(Sw // Bw, T.float32)
+    gath_codes, gath_scales = e(nw, T.int8), e(nw // Bw, T.float32)
+    y_layer = e(nw, T.float16)
+    send1_c, send1_s = e(ng // 2, T.uint8), e(ng // Bg, T.float32)
+    recv1_c, recv1_s = e(ng // 2, T.uint8), e(ng // Bg, T.float32)
+    send2_c, send2_s = e(chunk // 2, T.uint8), e(chunk // Bg, T.float32)
+    recv2_c, recv2_s = e(chunk // 2, T.uint8), e(chunk // Bg, T.float32)
+    y_grad = e(Sg, T.float16)
+
+    # simulated collectives, filled once
+    zpq.quant_i8(layer, Bw, out=(gath_codes, gath_scales))          # all-gather of 16 shards
+    zpq.qgz_reorder_quant_i4(grad, L, N, Bg, out=(send1_c, send1_s))
+    recv1_c.copy_(send1_c)
+    recv1_s.copy_(send1_s)                                          # hop-1 all-to-all
+    zpq.qgz_dequant_reduce_requant_i4(recv1_c, recv1_s, L, chunk, Bg, out=(send2_c, send2_s))
+    recv2_c.copy_(send2_c)
+    recv2_s.copy_(send2_s)                                          # hop-2 all-to-all
+    torch.cuda.synchronize()
+
+    kernels = [
+        ("K1 qwZ quant_i8 (shard 1/16, fp16, B=256)",
+         lambda: zpq.quant_i8(shard, Bw, out=(shard_codes, shard_scales)),
+         Sw * 2 + Sw + (Sw // Bw) * 4),
+        ("K2 qwZ dequant_i8 (gathered 16 shards -> fp16)",
+         lambda: zpq.dequant_i8(gath_codes, gath_scales, Bw, out=y_layer),
+         nw + (nw // Bw) * 4 + nw * 2),
+        ("K3 qgZ reorder_quant_i4 (fp16, L=8, N=48, B=64)",
+         lambda: zpq.qgz_reorder_quant_i4(grad, L, N, Bg, out=(send1_c, send1_s)),
+         ng * 2 + ng // 2 + (ng // Bg) * 4),
+        ("K4 qgZ hop-1 dequant_reduce_requant_i4 (8 x chunk -> INT4)",
+         lambda: zpq.qgz_dequant_reduce_requant_i4(recv1_c, recv1_s, L, chunk, Bg,
+                                                   out=(send2_c, send2_s)),
+         L * (chunk // 2 + (chunk // Bg) * 4) + chunk // 2 + (chunk // Bg) * 4),
+        ("K5 qgZ hop-2 dequant_reduce_average (48 x slice -> fp16)",
+         lambda: zpq.qgz_dequant_reduce_requant_i4(recv2_c, recv2_s, N, Sg, Bg,
+                                                   out_dtype=T.float16, divisor=float(W),
+                                                   out=y_grad),
+         N * (Sg // 2 + (Sg // Bg) * 4) + Sg * 2),
+    ]
+    step_bytes = sum(k[2] for k in kernels)
+
+    def step(events=None):
+        for i, (_, fn, _) in enumerate(kernels):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in kernels] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    per_kernel_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1])
+                                    for s in range(args.steps)])) for i in range(len(kernels))]
+
+    traffic = {}
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f)
+
+    rows = []
+    for (name, _, nbytes), ms in zip(kernels, per_kernel_ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows.append({"kernel": name, "bytes": nbytes, "us": round(ms * 1e3, 2),
+                     "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
+    dom = max(range(len(rows)), key=lambda i: per_kernel_ms[i])
+    dk = rows[dom]
+    tr = traffic.get(dk["kernel"].split(" ")[0])
+    roofline = {"bound": "hbm", "kernel": dk["kernel"], "achieved": dk["GBps"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["frac_of_peak"],
+                "traffic": tr}
+
+    check = None
+    if not args.no_check:
+        check = verify(zpq, synth, np, torch, layer_h, grad_h, gath_codes, gath_scales, y_layer,
+                       shard_codes, shard_scales, send1_c, send1_s, send2_c, send2_s, y_grad)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, layer_h, grad_h, args.cpu_fraction)
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "one rank's ZeRO++ quantized-communication step: qwZ on a GPT layer at "
+                        "hidden 8192 (fp16, INT8 block 256, 16 ranks) + qgZ on a 138B-model "
+                        "layer gradient (fp16, INT4 block 64, L=8, N=48, both hops)",
+            "qwz_layer_elems": nw, "qwz_shard_elems": Sw, "qgz_grad_elems": ng,
+            "step_bytes": step_bytes, "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+            "kernels": rows,
+            "parity": check,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def verify(zpq, synth, np, torch, layer_h, grad_h, gath_codes, gath_scales, y_layer, shard_codes,
+           shard_scales, send1_c, send1_s, send2_c, send2_s, y_grad):
+    """Sampled bit-exact check of this run's outputs against the oracle chain
+    computed from the generator's inputs (the parity tests do the same at
+    more samples)."""
+    import oracle
+    rng = np.random.default_rng(1234)
+    qw, qg = synth.QWZ_LAYER, synth.QGZ_FUSED
+    Bw, Sw = qw["block"], qw["n"] // qw["world"]
+    bl = np.unique(np.concatenate([[0], rng.integers(0, qw["n"] // Bw, 16)]))
+    xs = np.concatenate([layer_h[b * Bw:(b + 1) * Bw] for b in bl])
+    ec, es = oracle.quant_i8(xs, "f16", Bw)
+    ey = oracle.dequant_i8(ec, es, Bw, "f16")
+    gc = gath_codes.cpu().numpy()
+    gy = y_layer.view(torch.int16).cpu().numpy().view(np.uint16)
+    ok = np.array_equal(np.concatenate([gc[b * Bw:(b + 1) * Bw] for b in bl]), ec)
+    ok &= np.array_equal(np.concatenate([gy[b * Bw:(b + 1) * Bw] for b in bl]), ey.view(np.uint16))
+    sb = bl[bl < Sw // Bw]
+    sc = shard_codes.cpu().numpy()
+    ok &= np.array_equal(np.concatenate([sc[b * Bw:(b + 1) * Bw] for b in sb]),
+                         np.concatenate([ec[i * Bw:(i + 1) * Bw] for i, b in enumerate(bl)
+                                         if b < Sw // Bw]))
+    # qgZ: a few final blocks through the whole chain
+    L, N, B, n = qg["L"], qg["N"], qg["block"], qg["n"]
+    S, chunk = n // (L * N), n // L
+    ob = np.unique(rng.integers(0, S // B, 4))
+    src = oracle.reorder(np.arange(L * N, dtype=np.int64), L, N)
+    pos = np.array([i * chunk + m * S + b * B for m in range(N) for i in range(L) for b in ob])
+    start = src[pos // S] * S + pos % S
+    c1, s1 = oracle.qgz_reorder_quant_i4(np.concatenate([grad_h[s:s + B] for s in start]), "f16",
+                                         1, 1, B)
+    T = ob.size
+    cb = (B // 2) * T
+    c2 = []
+    s2 = []
+    for m in range(N):
+        rc, rs = oracle.qgz_dequant_reduce_requant_i4(c1[m * L * cb:(m + 1) * L * cb],
+                                                      s1[m * L * T:(m + 1) * L * T], L, T * B, B)
+        c2.append(rc)
+        s2.append(rs)
+    ey = oracle.qgz_dequant_reduce_requant_i4(np.concatenate(c2), np.concatenate(s2), N, T * B, B,
+                                              "f16", float(L * N))
+    yg = y_grad.view(torch.int16).cpu().numpy().view(np.uint16)
+    ok &= np.array_equal(np.concatenate([yg[b * B:(b + 1) * B] for b in ob]), ey.view(np.uint16))
+    s1g = send1_c.cpu().numpy()
+    ok &= np.array_equal(np.concatenate([s1g[p // 2:p // 2 + B // 2] for p in pos]), c1)
+    return {"sampled_blocks": int(bl.size + pos.size + ob.size), "bit_exact": bool(ok)}
+
+
+def cpu_baseline(np, layer_h, grad_h, frac):
+    """The oracle (plain single-threaded C) on a fraction of every kernel's
+    step work, same block sizes and the same L, N; GB/s over the same
+    algorithmic bytes as the GPU step."""
+    import oracle
+    import synth
+    qw, qg = synth.QWZ_LAYER, synth.QGZ_FUSED
+    Bw = qw["block"]
+    L, N, B = qg["L"], qg["N"], qg["block"]
+    W = L * N
+    n1 = int(qw["n"] // qw["world"] * frac) // Bw * Bw
+    n2 = int(qw["n"] * frac) // Bw * Bw
+    n3 = int(qg["n"] * frac) // (W * B) * (W * B)
+    c4, c5 = n3 // L, n3 // W
+    gc, gs = oracle.quant_i8(layer_h[:n2], "f16", Bw)        # K2's input: not timed
+
+    def timed(fn):
+        t = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t
+
+    secs = 0.0
+    _, dt = timed(lambda: oracle.quant_i8(layer_h[:n1], "f16", Bw))
+    secs += dt
+    _, dt = timed(lambda: oracle.dequant_i8(gc, gs, Bw, "f16"))
+    secs += dt
+    (c1, s1), dt = timed(lambda: oracle.qgz_reorder_quant_i4(grad_h[:n3], "f16", L, N, B))
+    secs += dt
+    (c2, s2), dt = timed(lambda: oracle.qgz_dequant_reduce_requant_i4(c1, s1, L, c4, B))
+    secs += dt
+    _, dt = timed(lambda: oracle.qgz_dequant_reduce_requant_i4(c2, s2, N, c5, B, "f16",
+                                                               float(W)))
+    secs += dt
+    nbytes = ((n1 * 2 + n1 + (n1 // Bw) * 4) + (n2 + (n2 // Bw) * 4 + n2 * 2) +
+              (n3 * 2 + n3 // 2 + (n3 // B) * 4) +
+              (L * (c4 // 2 + (c4 // B) * 4) + c4 // 2 + (c4 // B) * 4) +
+              (N * (c5 // 2 + (c5 // B) * 4) + c5 * 2))
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{frac:.4g} of every kernel's step work (qwZ shard {n1} and gathered "
+                      f"{n2} elements, qgZ gradient {n3} elements, hop-1 chunk {c4}, hop-2 "
+                      f"slice {c5}; same blocks, L, N); {secs:.1f} s of single-threaded oracle "
+                      f"time"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+"""libzpq's C ABI without a GPU: the library loads, exports every function
+declared in include/zpq.h, and rejects invalid arguments on the host before
+anything is launched (none of these calls reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_quantized_communication_amd as zpq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zpq.h")
+
+OK, NULL, SIZE, BLOCK, ALIGN, DTYPE, MODE, LAUNCH, ARG, ALIAS = range(10)
+P = 1 << 20        # fake, 16-byte aligned "device" addresses: never dereferenced
+NUL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:zpq_status|const char\*|int32_t)\s+(zpq_\w+)\s*\(", text, flags=re.M)
+
+
+def vp(x):
+    return ctypes.c_void_p(x)
+
+
+def test_exports_match_header():
+    names = declared_functions()
+    assert sorted(names) == sorted(zpq.EXPORTS)
+    L = zpq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert zpq.abi_version() == 1
+    text = open(HEADER).read()
+    assert "#define ZPQ_ABI_VERSION 1" in text
+    for s in range(10):
+        assert zpq.lib().zpq_status_str(s).decode() not in ("", "unknown status")
+    assert zpq.lib().zpq_status_str(99).decode() == "unknown status"
+
+
+def q8(x=P, dt=1, n=1024, block=256, codes=P + (1 << 16), scales=P + (1 << 18)):
+    return zpq.lib().zpq_quant_i8(vp(x), dt, n, block, vp(codes), vp(scales), NUL)
+
+
+def test_quant_i8_validation():
+    assert q8(block=100) == BLOCK
+    assert q8(block=16) == BLOCK
+    assert q8(n=1000) == SIZE
+    assert q8(n=-256) == SIZE
+    assert q8(dt=3) == DTYPE
+    assert q8(x=0) == NULL
+    assert q8(scales=0) == NULL
+    assert q8(x=P + 8) == ALIGN
+    assert q8(codes=P + 4) == ALIGN
+    assert q8(codes=P + 1024) == ALIAS          # codes inside x's 2 KB
+    assert q8(scales=P + (1 << 16) + 512) == ALIAS
+    assert q8(n=0, x=0, codes=0, scales=0) == OK   # empty: nothing to do
+
+
+def dq8(codes=P, scales=P + (1 << 16), n=1024, block=256, y=P + (1 << 18), dt=1):
+    return zpq.lib().zpq_dequant_i8(vp(codes), vp(scales), n, block, vp(y), dt, NUL)
+
+
+def test_dequant_i8_validation():
+    assert dq8(block=48) == BLOCK
+    assert dq8(n=1280 + 1) == SIZE
+    assert dq8(dt=7) == DTYPE
+    assert dq8(y=0) == NULL
+    assert dq8(scales=P + (1 << 16) + 4) == ALIGN
+    assert dq8(y=P + 512) == ALIAS
+    assert dq8(n=0, codes=0, scales=0, y=0) == OK
+
+
+def rq4(g=P, dt=2, n=8 * 4 * 128 * 3, L=8, N=4, block=128, codes=P + (1 << 18),
+        scales=P + (1 << 19)):
+    return zpq.lib().zpq_qgz_reorder_quant_i4(vp(g), dt, n, L, N, block, vp(codes), vp(scales),
+                                              NUL)
+
+
+def test_qgz_reorder_quant_validation():
+    assert rq4(block=127) == BLOCK
+    assert rq4(L=0) == ARG
+    assert rq4(N=-1) == ARG
+    assert rq4(n=8 * 4 * 128 * 3 + 128) == SIZE    # whole blocks but not whole slices
+    assert rq4(dt=-1) == DTYPE
+    assert rq4(g=0) == NULL
+    assert rq4(codes=P + (1 << 18) + 8) == ALIGN
+    assert rq4(codes=P + 4096) == ALIAS
+    assert rq4(n=0, g=0, codes=0, scales=0) == OK
+
+
+def dr4(ic=P, isc=P + (1 << 18), K=8, c=4096, block=128, oc=P + (1 << 19),
+        os_=P + (1 << 19) + (1 << 16), ov=0, odt=0, div=1.0):
+    return zpq.lib().zpq_qgz_dequant_reduce_requant_i4(vp(ic), vp(isc), K, c, block, vp(oc),
+                                                       vp(os_), vp(ov), odt,
+                                                       ctypes.c_float(div), NUL)
+
+
+def test_dequant_reduce_validation():
+    assert dr4(block=96) == BLOCK
+    assert dr4(K=0) == ARG
+    assert dr4(c=4096 + 64) == SIZE
+    assert dr4(c=1 << 32) == SIZE                    # per-lane offsets are 32-bit
+    # exactly one output mode
+    assert dr4(ov=P + (1 << 20)) == MODE              # both
+    assert dr4(oc=0, os_=0) == MODE                   # neither
+    assert dr4(os_=0) == MODE                         # half of I4
+    fl = dict(oc=0, os_=0, ov=P + (1 << 20))
+    assert dr4(odt=3, **fl) == DTYPE
+    assert dr4(div=0.0, **fl) == ARG
+    assert dr4(div=-2.0, **fl) == ARG
+    assert dr4(div=float("inf"), **fl) == ARG
+    assert dr4(div=float("nan"), **fl) == ARG
+    assert dr4(ic=0) == NULL
+    assert dr4(isc=P + (1 << 18) + 4) == ALIGN
+    assert dr4(oc=P + 512) == ALIAS                   # inside the received codes
+    assert dr4(ov=P + (1 << 18), oc=0, os_=0) == ALIAS
+    assert dr4(c=0, ic=0, isc=0) == OK
+
+
+def test_binding_refuses_bad_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1024, dtype=torch.float16)         # a CPU tensor
+    with pytest.raises(ValueError):
+        zpq.quant_i8(x, 256, out=(torch.zeros(1024, dtype=torch.int8),
+                                  torch.zeros(4, dtype=torch.float32)))

@@ -1,0 +1,209 @@
+"""GPU parity of every libzpq entry point against the CPU oracle, bit for bit,
+at sizes the oracle handles in seconds: several workgroup tiles plus a ragged
+tail, every element type and block size, adversarial blocks, edge cases."""
+import numpy as np
+import pytest
+
+import block_quantized_communication_amd as zpq
+import oracle
+from parity_util import (adversarial_f32, as_dtype, assert_bits_equal, from_device, to_device)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "f16", "bf16"]
+BLOCKS = [32, 64, 128, 256, 512]
+TILE = 256 * 16 * 2        # elements per workgroup of the quantize kernels
+
+
+def torch_dt(name):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("block", BLOCKS)
+def test_quant_i8(dtype, block):
+    rng = np.random.default_rng(block * 7 + len(dtype))
+    for nblocks in (1, 3, 2 * TILE // block + 5):          # ragged tails
+        n = nblocks * block
+        x = as_dtype(adversarial_f32(rng, n, block), dtype)
+        print(f"quant_i8 dtype={dtype} block={block} n={n}", flush=True)
+        codes, scales = zpq.quant_i8(to_device(x, dtype), block)
+        rc, rs = oracle.quant_i8(x, dtype, block)
+        assert_bits_equal(from_device(scales), rs, "scales")
+        assert_bits_equal(from_device(codes), rc, "codes")
+
+
+@pytest.mark.parametrize("out", DTYPES)
+@pytest.mark.parametrize("block", [32, 256, 512])
+def test_dequant_i8(out, block):
+    rng = np.random.default_rng(block + len(out))
+    n = (2 * TILE // block + 3) * block
+    codes = rng.integers(-128, 128, n).astype(np.int8)        # -128 too: any int8 decodes
+    s = rng.standard_normal(n // block).astype(np.float32) * np.float32(0.01)
+    s[::7] = 0.0
+    s[1::7] = np.float32(3e-41)                                # subnormal scales
+    s[2::7] = np.float32(2.6e36)                               # 127 * s near FLT_MAX
+    s[3::7] = np.abs(s[3::7]) * np.float32(1e-3)               # fp16-subnormal outputs
+    print(f"dequant_i8 out={out} block={block} n={n}", flush=True)
+    y = zpq.dequant_i8(to_device(codes), to_device(s), block, torch_dt(out))
+    assert_bits_equal(from_device(y), oracle.dequant_i8(codes, s, block, out), "values")
+
+
+def test_quant_dequant_roundtrip_f16_all_values():
+    """Every finite fp16 value inside blocks of every scale class."""
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    h = h[np.isfinite(h)]
+    h = h[: h.size - h.size % 256]
+    rng = np.random.default_rng(1)
+    x = rng.permutation(h)
+    codes, scales = zpq.quant_i8(to_device(x), 256)
+    rc, rs = oracle.quant_i8(x, "f16", 256)
+    assert_bits_equal(from_device(codes), rc, "codes")
+    assert_bits_equal(from_device(scales), rs, "scales")
+    y = zpq.dequant_i8(codes, scales, 256, torch_dt("f16"))
+    assert_bits_equal(from_device(y), oracle.dequant_i8(rc, rs, 256, "f16"), "dequant")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("block", [32, 64, 128, 512])
+@pytest.mark.parametrize("L,N", [(1, 1), (2, 2), (3, 2), (8, 4), (2, 5)])
+def test_qgz_reorder_quant_i4(dtype, block, L, N):
+    rng = np.random.default_rng(block + 10 * L + N)
+    W = L * N
+    for per_slice_blocks in (1, TILE // block + 3):          # slices shorter / longer than a tile
+        n = W * per_slice_blocks * block
+        x = as_dtype(adversarial_f32(rng, n, block), dtype)
+        print(f"reorder_quant_i4 dtype={dtype} block={block} L={L} N={N} n={n}", flush=True)
+        codes, scales = zpq.qgz_reorder_quant_i4(to_device(x, dtype), L, N, block)
+        rc, rs = oracle.qgz_reorder_quant_i4(x, dtype, L, N, block)
+        assert_bits_equal(from_device(scales), rs, "scales")
+        assert_bits_equal(from_device(codes), rc, "codes")
+
+
+def random_received(rng, K, chunk, block, huge=False):
+    """K received INT4 chunks: random nibbles and scales of every class.
+    Without `huge`, nibbles cover all 16 values (-8 included: any nibble
+    decodes).  With `huge`, some scales exceed FLT_MAX/8 (so 8*s overflows)
+    and nibbles stay in [-7, 7], as the quantizer produces, so that every true
+    sum stays finite."""
+    if huge:
+        q = rng.integers(-7, 8, K * chunk).astype(np.int8)
+        codes = ((q[0::2] & 0xF) | ((q[1::2] & 0xF) << 4)).astype(np.uint8)
+    else:
+        codes = rng.integers(0, 256, K * chunk // 2).astype(np.uint8)
+    nb = chunk // block
+    s = (np.abs(rng.standard_normal((K, nb))) * 10.0 ** rng.uniform(-4, 1, (K, 1))).astype(
+        np.float32)
+    s[:, ::9] = 0.0
+    s[:, 1::9] = np.float32(1e-40)
+    if huge:
+        s[0, 2::9] = np.float32(4.5e37)         # 8 * s overflows; 7 * s does not
+        s[1:, 2::9] = 0.0                        # keep the true sums finite
+    return codes, s.ravel()
+
+
+@pytest.mark.parametrize("block", BLOCKS)
+@pytest.mark.parametrize("K", [1, 2, 3, 5, 8, 16, 48])
+def test_dequant_reduce_requant_i4(block, K):
+    rng = np.random.default_rng(block * 100 + K)
+    chunk = (256 * 16 // block * 3 + 1) * block               # several tiles + ragged
+    for huge in (False, True):
+        if huge and K < 2:
+            continue
+        codes, s = random_received(rng, K, chunk, block, huge)
+        print(f"dequant_reduce_requant_i4 block={block} K={K} chunk={chunk} huge={huge}",
+              flush=True)
+        oc, os_ = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk,
+                                                     block)
+        rc, rs = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block)
+        assert_bits_equal(from_device(os_), rs, "scales")
+        assert_bits_equal(from_device(oc), rc, "codes")
+
+
+@pytest.mark.parametrize("out", DTYPES)
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("K,divisor", [(1, 1.0), (3, 3.0), (16, 16.0), (48, 384.0),
+                                       (8, 0.5), (5, 2.0 ** 50), (4, 1e-30)])
+def test_dequant_reduce_average(out, block, K, divisor):
+    rng = np.random.default_rng(block + K)
+    chunk = (256 * 16 // block * 2 + 3) * block
+    for huge in (False, True):
+        if huge and K < 2:
+            continue
+        codes, s = random_received(rng, K, chunk, block, huge)
+        print(f"dequant_reduce_average out={out} block={block} K={K} div={divisor} "
+              f"huge={huge}", flush=True)
+        y = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk, block,
+                                               out_dtype=torch_dt(out), divisor=divisor)
+        ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, out, divisor)
+        assert_bits_equal(from_device(y), ref, "values")
+
+
+def test_requant_single_source_is_identity():
+    """Hop-1 requantization of one source returns the quantizer's own codes
+    and scales (requantization is idempotent)."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_t(3, 128 * 999) * 1e-3).astype(np.float32)
+    codes, scales = zpq.qgz_reorder_quant_i4(to_device(x), 1, 1, 128)
+    oc, os_ = zpq.qgz_dequant_reduce_requant_i4(codes, scales, 1, x.size, 128)
+    assert_bits_equal(from_device(oc), from_device(codes), "codes")
+    assert_bits_equal(from_device(os_), from_device(scales), "scales")
+
+
+def test_empty_inputs_are_noops():
+    import torch
+    e = torch.empty(0, device="cuda")
+    c, s = zpq.quant_i8(e.half(), 256)
+    assert c.numel() == 0 and s.numel() == 0
+    y = zpq.dequant_i8(c, s, 256, torch.float16)
+    assert y.numel() == 0
+
+
+def test_outputs_untouched_outside_range():
+    """Canaries around every output: nothing is written past the end."""
+    import torch
+    rng = np.random.default_rng(5)
+    n, block = 3 * 256 + 4096, 256
+    x = to_device(as_dtype(adversarial_f32(rng, n, block), "f16"))
+    guard = 4096
+    cbuf = torch.full((n + 2 * guard,), 0x5A, dtype=torch.int8, device="cuda")
+    sbuf = torch.full((n // block + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    zpq.quant_i8(x, block, out=(cbuf[guard:guard + n], sbuf[guard:guard + n // block]))
+    torch.cuda.synchronize()
+    assert (cbuf[:guard] == 0x5A).all() and (cbuf[guard + n:] == 0x5A).all()
+    assert (sbuf[:guard] == 7.0).all() and (sbuf[guard + n // block:] == 7.0).all()
+    # INT4 paths
+    g = to_device(as_dtype(adversarial_f32(rng, 8 * 4 * 128 * 3, 128), "bf16"), "bf16")
+    m = g.numel()
+    cb = torch.full((m // 2 + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    sb = torch.full((m // 128 + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    zpq.qgz_reorder_quant_i4(g, 8, 4, 128, out=(cb[guard:guard + m // 2],
+                                                sb[guard:guard + m // 128]))
+    torch.cuda.synchronize()
+    assert (cb[:guard] == 0xA5).all() and (cb[guard + m // 2:] == 0xA5).all()
+    assert (sb[:guard] == 7.0).all() and (sb[guard + m // 128:] == 7.0).all()
+    chunk = m // 8
+    ob = torch.full((chunk // 2 + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    osb = torch.full((chunk // 128 + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    zpq.qgz_dequant_reduce_requant_i4(cb[guard:guard + m // 2], sb[guard:guard + m // 128], 8,
+                                       chunk, 128, out=(ob[guard:guard + chunk // 2],
+                                                        osb[guard:guard + chunk // 128]))
+    vb = torch.full((chunk + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    zpq.qgz_dequant_reduce_requant_i4(cb[guard:guard + m // 2], sb[guard:guard + m // 128], 8,
+                                       chunk, 128, out_dtype=torch.float32, divisor=8.0,
+                                       out=vb[guard:guard + chunk])
+    torch.cuda.synchronize()
+    assert (ob[:guard] == 0xA5).all() and (ob[guard + chunk // 2:] == 0xA5).all()
+    assert (osb[:guard] == 7.0).all() and (osb[guard + chunk // 128:] == 7.0).all()
+    assert (vb[:guard] == 7.0).all() and (vb[guard + chunk:] == 7.0).all()
+
+
+def test_deterministic_repeat():
+    import torch
+    rng = np.random.default_rng(8)
+    g = to_device(as_dtype(adversarial_f32(rng, 8 * 48 * 64 * 5, 64), "f16"))
+    a = zpq.qgz_reorder_quant_i4(g, 8, 48, 64)
+    b = zpq.qgz_reorder_quant_i4(g, 8, 48, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
