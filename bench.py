@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--cpu-fraction", type=float, default=1.0 / 16)
+    ap.add_argument("--cpu-fraction", type=float, default=0.5)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-kernel HBM bytes from rocprofv3 counters (optional)")
     return ap.parse_args()
