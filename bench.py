@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.5)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy 1 GiB with torch (a plain copy kernel of known "
+                         "size, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-kernel HBM bytes from rocprofv3 counters (optional)")
     return ap.parse_args()
@@ -149,10 +152,25 @@ def main():
     per_kernel_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1])
                                     for s in range(args.steps)])) for i in range(len(kernels))]
 
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
+    # valid only for the kernel source they were measured on
     traffic = {}
     if args.traffic and os.path.exists(args.traffic):
+        import hashlib
         with open(args.traffic) as f:
-            traffic = json.load(f)
+            t = json.load(f)
+        src = os.path.join(ROOT, "block_quantized_communication_amd", "csrc", "zpq.hip")
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() == t.get("source_sha256"):
+                traffic = t.get("bytes_per_launch", {})
 
     rows = []
     for (name, _, nbytes), ms in zip(kernels, per_kernel_ms):
