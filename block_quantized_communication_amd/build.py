@@ -20,7 +20,7 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=off",
-    "-Wall", "-Wno-unused-function",
+    "-fconstexpr-steps=100000000", "-Wall", "-Wno-unused-function",
 ]
 
 

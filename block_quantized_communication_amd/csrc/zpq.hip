@@ -33,9 +33,98 @@
 
 #include "zpq.h"
 
+// Launch shapes.  Defaults are the measured best on MI355X; each can be
+// overridden at build time (-DZPQ_...) to compare variants.
+#ifndef ZPQ_QUANT_EPL
+#define ZPQ_QUANT_EPL 8        // elements per lane, INT8 quantize of fp16/bf16 (block <= 256)
+#endif
+#ifndef ZPQ_QUANT_U
+#define ZPQ_QUANT_U 2          // tiles per lane, INT8 quantize
+#endif
+#ifndef ZPQ_DEQUANT_EPL
+#define ZPQ_DEQUANT_EPL 8      // elements per lane, INT8 dequantize
+#endif
+#ifndef ZPQ_DEQUANT_U
+#define ZPQ_DEQUANT_U 1
+#endif
+#ifndef ZPQ_QGZ_EPL
+#define ZPQ_QGZ_EPL 8          // elements per lane, reorder + INT4 quantize of fp16/bf16
+#endif
+#ifndef ZPQ_QGZ_U
+#define ZPQ_QGZ_U 4            // tiles per lane, reorder + INT4 quantize
+#endif
+#ifndef ZPQ_REDUCE_EPL_I4
+#define ZPQ_REDUCE_EPL_I4 16   // elements per lane, hop-1 receive (INT4 out)
+#endif
+#ifndef ZPQ_REDUCE_EPL_FL
+#define ZPQ_REDUCE_EPL_FL 16   // elements per lane, hop-2 receive (float out)
+#endif
+#ifndef ZPQ_REDUCE_PF_I4
+#define ZPQ_REDUCE_PF_I4 4     // received sources in flight per lane (hop 1)
+#endif
+#ifndef ZPQ_REDUCE_PF_FL
+#define ZPQ_REDUCE_PF_FL 8     // received sources in flight per lane (hop 2)
+#endif
+// Persistent grids: workgroups per compute unit (0 = one workgroup per
+// virtual block, no loop).
+#ifndef ZPQ_PERSIST_QUANT
+#define ZPQ_PERSIST_QUANT 0
+#endif
+#ifndef ZPQ_PERSIST_DEQUANT
+#define ZPQ_PERSIST_DEQUANT 0
+#endif
+#ifndef ZPQ_PERSIST_QGZ
+#define ZPQ_PERSIST_QGZ 0
+#endif
+#ifndef ZPQ_PERSIST_REDUCE
+#define ZPQ_PERSIST_REDUCE 0
+#endif
+#ifndef ZPQ_THREADS
+#define ZPQ_THREADS 256
+#endif
+
+// Non-temporal hints on streamed loads (L) and stores (S), per kernel.
+#ifndef ZPQ_NTL_QUANT
+#define ZPQ_NTL_QUANT 1
+#endif
+#ifndef ZPQ_NTS_QUANT
+#define ZPQ_NTS_QUANT 0
+#endif
+#ifndef ZPQ_NTL_DEQUANT
+#define ZPQ_NTL_DEQUANT 1
+#endif
+#ifndef ZPQ_NTS_DEQUANT
+#define ZPQ_NTS_DEQUANT 0
+#endif
+#ifndef ZPQ_NTL_QGZ
+#define ZPQ_NTL_QGZ 1
+#endif
+#ifndef ZPQ_NTS_QGZ
+#define ZPQ_NTS_QGZ 1
+#endif
+#ifndef ZPQ_NTL_REDUCE
+#define ZPQ_NTL_REDUCE 1
+#endif
+#ifndef ZPQ_NTS_REDUCE
+#define ZPQ_NTS_REDUCE 1
+#endif
+
 namespace {
 
-constexpr int kThreads = 256;          // 4 waves of 64 per workgroup
+constexpr int kThreads = ZPQ_THREADS;  // 4 waves of 64 per workgroup by default
+
+// Streamed (read-once / write-once) accesses, with or without the
+// non-temporal hint.
+template <bool NT, class T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT, class T>
+__device__ __forceinline__ void st_stream(T v, T* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -90,30 +179,126 @@ __device__ __forceinline__ uint32_t round_code(float t) {
     return __float_as_uint(t + 12582912.0f);
 }
 
-// Per-block quantizer state: scale s = fl32(a / QMAX) (IEEE division) and,
-// when s >= 2^-100, its correctly rounded reciprocal for div_cr.
-template <int QMAX>
+// fl32(x / s) after ONE residual correction.  For fp16 and bf16 inputs
+// (x and the block absmax both 16-bit values) this rounds to the same integer
+// code as the IEEE quotient: checked by exhaustion over every absmax and
+// every |x| <= absmax of both types, for qmax 127 and 7.
+__device__ __forceinline__ float div_1c(float x, float s, float r) {
+    const float q = x * r;
+    return __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+}
+
+// Round-half-even without the clamp, for the fast path: with a normal scale
+// s = fl32(a/QMAX) every |x| <= a has |fl32(x/s)| <= fl32(a/s) <= QMAX(1 + 2^-23),
+// which rounds to at most QMAX.
+__device__ __forceinline__ uint32_t round_code_fast(float t) {
+    return __float_as_uint(t + 12582912.0f);
+}
+
+// Per-block quantizer state: scale s = fl32(a / QMAX) and, when
+// s >= 2^-100, its correctly rounded reciprocal for the division above.
+// The scale uses the corrected division by the constant QMAX (exact for
+// a >= 2^-90, where no residual underflows), else the IEEE operator.
+// ONE_STEP selects div_1c for the codes (16-bit inputs only).
+template <int QMAX, bool ONE_STEP>
 struct BlockScale {
     float s, r;
     bool fast;
+    BlockScale() = default;
+    // From a precomputed (s, fl32(1/s)) pair; r == 0 marks the slow path.
+    __device__ __forceinline__ BlockScale(float s_, float r_) : s(s_), r(r_), fast(r_ != 0.0f) {}
     __device__ __forceinline__ explicit BlockScale(float a) {
-        s = a / (float)QMAX;
+        constexpr float kInvQ = 1.0f / (float)QMAX;      // fl32(1/QMAX), folded by the compiler
+        if (a >= 0x1p-90f) s = div_cr(a, (float)QMAX, kInvQ);
+        else s = a / (float)QMAX;
         fast = s >= 0x1p-100f;
         r = fast ? 1.0f / s : 0.0f;
     }
-    // Codes of N values (in place into bit patterns).  The slow path (tiny
-    // or zero scale, block-uniform) divides with the IEEE operator.
+    // Codes of N values (as rounded bit patterns).  The slow path (tiny or
+    // zero scale, block-uniform) divides with the IEEE operator.
     template <int N>
     __device__ __forceinline__ void codes(const float (&v)[N], uint32_t (&out)[N]) const {
         if (fast) {
 #pragma unroll
-            for (int k = 0; k < N; ++k) out[k] = round_code<QMAX>(div_cr(v[k], s, r));
+            for (int k = 0; k < N; ++k)
+                out[k] = round_code_fast(ONE_STEP ? div_1c(v[k], s, r) : div_cr(v[k], s, r));
         } else {
 #pragma unroll
             for (int k = 0; k < N; ++k) out[k] = round_code<QMAX>(s != 0.0f ? v[k] / s : 0.0f);
         }
     }
 };
+
+// ---------------------------------------------------------------------------
+// Scale tables for 16-bit inputs.  The block absmax a of fp16 or bf16 data is
+// a 16-bit value m * 2^k (m its integer significand).  While a/QMAX and its
+// reciprocal stay normal floats, fl32(a/QMAX) = fl32(m/QMAX) * 2^k and
+// fl32(1/s) = fl32(1/fl32(m/QMAX)) * 2^-k exactly, so a table indexed by the
+// significand (folded at compile time: the compiler evaluates the IEEE
+// divisions) plus two exact v_ldexp_f32 give s and 1/s.  The tables are small
+// (fp16: 2048 entries, bf16: 128) so lookups hit in the per-CU cache.
+struct ScaleRecip {
+    float s, r;
+};
+
+template <int QMAX, int N, int LEAD>
+struct MantTable {
+    ScaleRecip e[N];
+};
+
+// entry i: significand LEAD + i for i < N1, else (fp16 subnormals) i - N1
+template <int QMAX, int N, int LEAD, int N1>
+constexpr MantTable<QMAX, N, LEAD> make_mant_table() {
+    MantTable<QMAX, N, LEAD> t{};
+    for (int i = 0; i < N; ++i) {
+        const float m = i < N1 ? (float)(LEAD + i) : (float)(i - N1);
+        const float sc = m / (float)QMAX;
+        t.e[i].s = sc;
+        t.e[i].r = sc != 0.0f ? 1.0f / sc : 0.0f;
+    }
+    return t;
+}
+
+// fp16: normal a = (1024 + M) * 2^(E-25); subnormal a = M * 2^-24
+__device__ constexpr MantTable<127, 2048, 1024> kF16Q127 = make_mant_table<127, 2048, 1024, 1024>();
+__device__ constexpr MantTable<7, 2048, 1024> kF16Q7 = make_mant_table<7, 2048, 1024, 1024>();
+// bf16: normal a = (128 + M) * 2^(E-134)
+__device__ constexpr MantTable<127, 128, 128> kBF16Q127 = make_mant_table<127, 128, 128, 128>();
+__device__ constexpr MantTable<7, 128, 128> kBF16Q7 = make_mant_table<7, 128, 128, 128>();
+
+template <int DT, int QMAX>
+__device__ __forceinline__ const ScaleRecip* mant_table() {
+    if constexpr (DT == ZPQ_F16) return QMAX == 127 ? kF16Q127.e : kF16Q7.e;
+    else return QMAX == 127 ? kBF16Q127.e : kBF16Q7.e;
+}
+
+// (s, 1/s) of a 16-bit absmax pattern h (sign cleared); r == 0 when the block
+// needs the slow path, and then s is exact (IEEE division) or 0 for a
+// non-finite absmax (outside the domain).
+template <int DT, int QMAX>
+__device__ __forceinline__ ScaleRecip scale_of16(uint32_t h) {
+    ScaleRecip out;
+    if constexpr (DT == ZPQ_F16) {
+        const uint32_t E = h >> 10, M = h & 0x3FFu;
+        const ScaleRecip t = mant_table<DT, QMAX>()[E ? M : 1024u + M];
+        const int k = E ? (int)E - 25 : -24;        // fp16 scales are always normal
+        out.s = __builtin_amdgcn_ldexpf(t.s, k);
+        out.r = __builtin_amdgcn_ldexpf(t.r, -k);
+        if (E == 31) out.s = out.r = 0.0f;
+    } else {
+        const uint32_t E = h >> 7, M = h & 0x7Fu;
+        const ScaleRecip t = mant_table<DT, QMAX>()[M];
+        const int k = (int)E - 134;
+        out.s = __builtin_amdgcn_ldexpf(t.s, k);
+        out.r = __builtin_amdgcn_ldexpf(t.r, -k);
+        if (!(out.s >= 0x1p-100f) || E == 0 || E == 255) {
+            // tiny or non-finite absmax: exact scale, slow path
+            out.s = E == 255 ? 0.0f : __uint_as_float(h << 16) / (float)QMAX;
+            out.r = 0.0f;
+        }
+    }
+    return out;
+}
 
 // ---------------------------------------------------------------------------
 // Byte packing with v_perm_b32.  perm(a, b, sel): selector byte 0..3 picks a
@@ -133,17 +318,19 @@ __device__ __forceinline__ uint32_t pack_nibbles(const uint32_t* c) {
 }
 
 // EPL/8 dwords of packed nibbles (EPL/2 bytes) to a 8- or 16-byte aligned address.
-template <int EPL>
+template <int EPL, bool NT>
 __device__ __forceinline__ void store_nibbles(uint8_t* dst, const uint32_t* packed) {
-    if constexpr (EPL == 16) {
-        __builtin_nontemporal_store(u32x2{packed[0], packed[1]}, reinterpret_cast<u32x2*>(dst));
+    if constexpr (EPL == 8) {
+        st_stream<NT>(packed[0], reinterpret_cast<uint32_t*>(dst));
+    } else if constexpr (EPL == 16) {
+        st_stream<NT>(u32x2{packed[0], packed[1]}, reinterpret_cast<u32x2*>(dst));
     } else {
         static_assert(EPL % 32 == 0, "16-byte stores");
 #pragma unroll
         for (int k = 0; k < EPL / 32; ++k)
-            __builtin_nontemporal_store(u32x4{packed[4 * k], packed[4 * k + 1], packed[4 * k + 2],
-                                              packed[4 * k + 3]},
-                                        reinterpret_cast<u32x4*>(dst) + k);
+            st_stream<NT>(u32x4{packed[4 * k], packed[4 * k + 1], packed[4 * k + 2],
+                                packed[4 * k + 3]},
+                          reinterpret_cast<u32x4*>(dst) + k);
     }
 }
 
@@ -158,12 +345,13 @@ struct InTile {
     static_assert(WORDS % 4 == 0, "whole 16-byte vectors");
     uint32_t w[WORDS];
 
+    template <bool NT>
     __device__ __forceinline__ void load(const void* base, int64_t elem) {
         const u32x4* p = reinterpret_cast<const u32x4*>(
             static_cast<const char*>(base) + elem * ElemBytes<DT>::v);
 #pragma unroll
         for (int i = 0; i < WORDS / 4; ++i) {
-            u32x4 t = __builtin_nontemporal_load(p + i);
+            u32x4 t = ld_stream<NT>(p + i);
             w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
         }
     }
@@ -179,6 +367,29 @@ struct InTile {
             return __half2float(__ushort_as_half((unsigned short)h));
         } else {
             return __uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
+        }
+    }
+    // 15-bit magnitude pattern of max |x| over the tile (16-bit types only)
+    __device__ __forceinline__ uint32_t absmax16() const {
+        static_assert(DT != ZPQ_F32, "16-bit inputs");
+        u16x2 m = {0, 0};
+#pragma unroll
+        for (int i = 0; i < WORDS; ++i) {
+            const uint32_t a = w[i] & 0x7FFF7FFFu;
+            const u16x2 v = {(unsigned short)(a & 0xFFFFu), (unsigned short)(a >> 16)};
+            m = __builtin_elementwise_max(m, v);
+        }
+        return m.x > m.y ? m.x : m.y;
+    }
+    // The block's quantizer state; every lane of the aligned group of G lanes
+    // holding the block gets the same one.
+    template <int QMAX, int G>
+    __device__ __forceinline__ BlockScale<QMAX, DT != ZPQ_F32> block_scale() const {
+        if constexpr (DT == ZPQ_F32) {
+            return BlockScale<QMAX, false>(__uint_as_float(group_max<G>(absmax_bits())));
+        } else {
+            const ScaleRecip sr = scale_of16<DT, QMAX>(group_max<G>(absmax16()));
+            return BlockScale<QMAX, true>(sr.s, sr.r);
         }
     }
     // bit pattern of max |x| over the tile, as fp32
@@ -214,20 +425,25 @@ struct InTile {
 template <int DT, int BLOCK, int EPL, int U>
 __global__ __launch_bounds__(kThreads) void k_quant_i8(const void* __restrict__ x, int64_t n,
                                                        int8_t* __restrict__ codes,
-                                                       float* __restrict__ scales) {
+                                                       float* __restrict__ scales, uint32_t nvb) {
     constexpr int G = BLOCK / EPL;
-    const int64_t wg_base = (int64_t)blockIdx.x * (U * kThreads * EPL);
+    for (uint32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+    const int64_t wg_base = (int64_t)vb * (U * kThreads * EPL);
     InTile<DT, EPL> tile[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t e = wg_base + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
-        if (e < n) tile[u].load(x, e); else tile[u].zero();
+        if (e < n) tile[u].template load<ZPQ_NTL_QUANT>(x, e); else tile[u].zero();
     }
+    // Every tile's block scale first, so that the scale-table loads of all
+    // tiles are in flight together, then the codes.
+    BlockScale<127, DT != ZPQ_F32> bss[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) bss[u] = tile[u].template block_scale<127, G>();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t e = wg_base + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
-        const float a = __uint_as_float(group_max<G>(tile[u].absmax_bits()));
-        BlockScale<127> bs(a);
+        const auto& bs = bss[u];
         float v[EPL];
 #pragma unroll
         for (int k = 0; k < EPL; ++k) v[k] = tile[u].get(k);
@@ -238,25 +454,30 @@ __global__ __launch_bounds__(kThreads) void k_quant_i8(const void* __restrict__ 
 #pragma unroll
             for (int k = 0; k < EPL / 4; ++k)
                 packed[k] = pack_low_bytes(q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]);
+            if constexpr (EPL == 8) {
+                st_stream<ZPQ_NTS_QUANT>(u32x2{packed[0], packed[1]},
+                                         reinterpret_cast<u32x2*>(codes + e));
+            }
             u32x4* dst = reinterpret_cast<u32x4*>(codes + e);
 #pragma unroll
             for (int k = 0; k < EPL / 16; ++k)
-                __builtin_nontemporal_store(u32x4{packed[4 * k], packed[4 * k + 1],
+                st_stream<ZPQ_NTS_QUANT>(u32x4{packed[4 * k], packed[4 * k + 1],
                                                   packed[4 * k + 2], packed[4 * k + 3]}, dst + k);
             if ((threadIdx.x & (G - 1)) == 0) scales[e / BLOCK] = bs.s;
         }
+    }
     }
 }
 
 // ---------------------------------------------------------------------------
 // K2: qwZ INT8 dequantize into fp32 / fp16 / bf16.
-template <int OT, int EPL>
+template <int OT, int EPL, bool NT>
 __device__ __forceinline__ void store_out(void* __restrict__ y, int64_t e, const float (&v)[EPL]) {
     if constexpr (OT == ZPQ_F32) {
         u32x4* dst = reinterpret_cast<u32x4*>(static_cast<float*>(y) + e);
 #pragma unroll
         for (int k = 0; k < EPL / 4; ++k)
-            __builtin_nontemporal_store(
+            st_stream<NT>(
                 u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
                       __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])},
                 dst + k);
@@ -283,7 +504,7 @@ __device__ __forceinline__ void store_out(void* __restrict__ y, int64_t e, const
         u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + e);
 #pragma unroll
         for (int k = 0; k < EPL / 8; ++k)
-            __builtin_nontemporal_store(u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]},
+            st_stream<NT>(u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]},
                                         dst + k);
     }
 }
@@ -291,16 +512,26 @@ __device__ __forceinline__ void store_out(void* __restrict__ y, int64_t e, const
 template <int OT, int BLOCK, int EPL, int U>
 __global__ __launch_bounds__(kThreads) void k_dequant_i8(const int8_t* __restrict__ codes,
                                                          const float* __restrict__ scales,
-                                                         int64_t n, void* __restrict__ y) {
-    static_assert(EPL == 16, "one 16-byte code vector per lane and tile");
-    const int64_t wg_base = (int64_t)blockIdx.x * (U * kThreads * EPL);
-    u32x4 cw[U];
+                                                         int64_t n, void* __restrict__ y,
+                                                         uint32_t nvb) {
+    static_assert((EPL == 8 || EPL % 16 == 0) && EPL <= BLOCK, "code vectors inside a block");
+    constexpr int V = EPL >= 16 ? EPL / 16 : 1;
+    for (uint32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+    const int64_t wg_base = (int64_t)vb * (U * kThreads * EPL);
+    u32x4 cw[U][V];
     float s[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t e = wg_base + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
         if (e < n) {
-            cw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + e));
+            if constexpr (EPL == 8) {
+                const u32x2 t = ld_stream<ZPQ_NTL_DEQUANT>(reinterpret_cast<const u32x2*>(codes + e));
+                cw[u][0] = u32x4{t.x, t.y, 0u, 0u};
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    cw[u][v] = ld_stream<ZPQ_NTL_DEQUANT>(reinterpret_cast<const u32x4*>(codes + e) + v);
+            }
             s[u] = scales[e / BLOCK];
         }
     }
@@ -308,15 +539,17 @@ __global__ __launch_bounds__(kThreads) void k_dequant_i8(const int8_t* __restric
     for (int u = 0; u < U; ++u) {
         const int64_t e = wg_base + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
         if (e < n) {
-            const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
             float v[EPL];
 #pragma unroll
             for (int k = 0; k < EPL; ++k) {
-                const int8_t q = (int8_t)(w[k >> 2] >> (8 * (k & 3)));
+                const u32x4 c = cw[u][k >> 4];
+                const uint32_t w = c[(k >> 2) & 3];
+                const int8_t q = (int8_t)(w >> (8 * (k & 3)));
                 v[k] = (float)q * s[u];
             }
-            store_out<OT, EPL>(y, e, v);
+            store_out<OT, EPL, ZPQ_NTS_DEQUANT>(y, e, v);
         }
+    }
     }
 }
 
@@ -328,10 +561,11 @@ __global__ __launch_bounds__(kThreads) void k_dequant_i8(const int8_t* __restric
 template <int DT, int BLOCK, int EPL, int U>
 __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
     const void* __restrict__ grad, int64_t S, int32_t L, int32_t N, uint32_t wgs_per_slice,
-    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+    uint8_t* __restrict__ codes, float* __restrict__ scales, uint32_t nvb) {
     constexpr int G = BLOCK / EPL;
-    const uint32_t p = blockIdx.x / wgs_per_slice;
-    const uint32_t w = blockIdx.x - p * wgs_per_slice;
+    for (uint32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+    const uint32_t p = vb / wgs_per_slice;
+    const uint32_t w = vb - p * wgs_per_slice;
     const uint32_t j = p / (uint32_t)N;
     const uint32_t m = p - j * (uint32_t)N;
     const int64_t src0 = ((int64_t)m * L + j) * S;      // first element of slice m*L + j
@@ -341,13 +575,17 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t f = f0 + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
-        if (f < S) tile[u].load(grad, src0 + f); else tile[u].zero();
+        if (f < S) tile[u].template load<ZPQ_NTL_QGZ>(grad, src0 + f); else tile[u].zero();
     }
+    // Every tile's block scale first, so that the scale-table loads of all
+    // tiles are in flight together, then the codes.
+    BlockScale<7, DT != ZPQ_F32> bss[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) bss[u] = tile[u].template block_scale<7, G>();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t f = f0 + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
-        const float a = __uint_as_float(group_max<G>(tile[u].absmax_bits()));
-        BlockScale<7> bs(a);
+        const auto& bs = bss[u];
         float v[EPL];
 #pragma unroll
         for (int k = 0; k < EPL; ++k) v[k] = tile[u].get(k);
@@ -358,9 +596,10 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
             uint32_t packed[EPL / 8];
 #pragma unroll
             for (int k = 0; k < EPL / 8; ++k) packed[k] = pack_nibbles(q + 8 * k);
-            store_nibbles<EPL>(codes + e / 2, packed);
+            store_nibbles<EPL, ZPQ_NTS_QGZ>(codes + e / 2, packed);
             if ((threadIdx.x & (G - 1)) == 0) scales[e / BLOCK] = bs.s;
         }
+    }
     }
 }
 
@@ -382,21 +621,38 @@ struct SrcCodes {
     float s;
 };
 
-// Source base pointers are wave-uniform (SGPRs); per-lane offsets are 32-bit.
+// Received sources are read through buffer descriptors: the source's base
+// address lives in SGPRs (advanced per source by scalar adds) and each lane
+// supplies only a 32-bit byte offset, so the source loop spends no vector
+// instructions on addresses.  A descriptor covers exactly one source's chunk
+// (codes) or scale vector; an offset past it would read zeros, not fault.
+// Word 3 0x00020000 is the raw-buffer format for the gfx9 family.
+// Cache-policy operand of the code loads: 2 is the non-temporal bit.
+constexpr int kAuxReduce = ZPQ_NTL_REDUCE ? 2 : 0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
 template <int EPL>
-__device__ __forceinline__ void load_src(SrcCodes<EPL>& d, const uint8_t* cbase, uint32_t coff,
-                                         const float* sbase, uint32_t soff) {
-    if constexpr (EPL == 16) {
-        u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(cbase + coff));
-        d.w[0] = t.x; d.w[1] = t.y;
+__device__ __forceinline__ void load_src(SrcCodes<EPL>& d, const uint8_t* cbase, uint32_t cbytes,
+                                         uint32_t coff, const float* sbase, uint32_t sbytes,
+                                         uint32_t soff) {
+    const __amdgpu_buffer_rsrc_t rc = rsrc(cbase, cbytes);
+    if constexpr (EPL == 8) {
+        d.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, coff, 0, kAuxReduce);
+    } else if constexpr (EPL == 16) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b64(rc, coff, 0, kAuxReduce);
+        d.w[0] = t[0]; d.w[1] = t[1];
     } else {
 #pragma unroll
         for (int i = 0; i < EPL / 32; ++i) {
-            u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + coff) + i);
-            d.w[4 * i] = t.x; d.w[4 * i + 1] = t.y; d.w[4 * i + 2] = t.z; d.w[4 * i + 3] = t.w;
+            const auto t = __builtin_amdgcn_raw_buffer_load_b128(rc, coff + 16 * i, 0, kAuxReduce);
+            d.w[4 * i] = t[0]; d.w[4 * i + 1] = t[1]; d.w[4 * i + 2] = t[2]; d.w[4 * i + 3] = t[3];
         }
     }
-    d.s = sbase[soff];
+    d.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(sbase, sbytes), soff * 4, 0, 0));
 }
 
 // Byte k of x as a float, one v_cvt_f32_ubyte{k}.  Written as asm so the
@@ -418,9 +674,9 @@ __device__ __forceinline__ void accumulate(float (&acc)[EPL], const SrcCodes<EPL
     const float c = s * -8.0f;
 #pragma unroll
     for (int i = 0; i < SrcCodes<EPL>::W; ++i) {
-        const uint32_t b = d.w[i] ^ 0x88888888u;          // nibble q -> q + 8
-        const uint32_t lo = b & 0x0F0F0F0Fu;               // byte k: element 8i + 2k
-        const uint32_t hi = (b >> 4) & 0x0F0F0F0Fu;        // byte k: element 8i + 2k + 1
+        // nibble q -> q + 8 by flipping its top bit (one 3-input bit op each)
+        const uint32_t lo = (d.w[i] & 0x0F0F0F0Fu) ^ 0x08080808u;          // byte k: element 8i+2k
+        const uint32_t hi = ((d.w[i] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // byte k: element 8i+2k+1
         float ul[4], uh[4];
         ul[0] = cvt_ubyte<0>(lo); uh[0] = cvt_ubyte<0>(hi);
         ul[1] = cvt_ubyte<1>(lo); uh[1] = cvt_ubyte<1>(hi);
@@ -446,37 +702,70 @@ __device__ __forceinline__ void accumulate_direct(float (&acc)[EPL], const SrcCo
     }
 }
 
+template <int BLOCK, int EPL, int OUT, int PF>
+__device__ __forceinline__ void reduce_tile(
+    const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
+    int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
+    void* __restrict__ out_vals, float divisor, float rdiv, bool div_fast, int64_t e);
+
 template <int BLOCK, int EPL, int OUT /* -1: INT4, else a zpq_dtype */, int PF>
 __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
-    void* __restrict__ out_vals, float divisor, float rdiv, bool div_fast) {
+    void* __restrict__ out_vals, float divisor, float rdiv, bool div_fast, uint32_t nvb) {
+    for (uint32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+        const int64_t e = ((int64_t)vb * kThreads + threadIdx.x) * EPL;
+        if (e < c)                 // whole quantization blocks leave together
+            reduce_tile<BLOCK, EPL, OUT, PF>(in_codes, in_scales, K, c, out_codes, out_scales,
+                                             out_vals, divisor, rdiv, div_fast, e);
+    }
+}
+
+template <int BLOCK, int EPL, int OUT, int PF>
+__device__ __forceinline__ void reduce_tile(
+    const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
+    int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
+    void* __restrict__ out_vals, float divisor, float rdiv, bool div_fast, int64_t e) {
     constexpr int G = BLOCK / EPL;
-    const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * EPL;
-    if (e >= c) return;            // whole quantization blocks leave together
     const int64_t cstride = c / 2, sstride = c / BLOCK;
     const uint32_t coff = (uint32_t)(e / 2), soff = (uint32_t)(e / BLOCK);   // c < 2^32
+    const uint32_t cbytes = (uint32_t)cstride, sbytes = (uint32_t)(sstride * 4);
 
     float acc[EPL];
 #pragma unroll
     for (int k = 0; k < EPL; ++k) acc[k] = 0.0f;
 
-    // PF sources in flight: slot k holds source i0 + k
-    SrcCodes<EPL> buf[PF];
+    // Sources in flight.  The steady-state loop refills every slot without a
+    // condition (a whole group of PF sources always remains), so the
+    // compiler can wait for exactly the oldest load instead of all of them.
+    auto src_load = [&](SrcCodes<EPL>& d, int i) {
+        load_src<EPL>(d, in_codes + (int64_t)i * cstride, cbytes, coff,
+                      in_scales + (int64_t)i * sstride, sbytes, soff);
+    };
+    if (K >= PF) {
+        SrcCodes<EPL> buf[PF];
 #pragma unroll
-    for (int k = 0; k < PF; ++k)
-        if (k < K) load_src<EPL>(buf[k], in_codes + k * cstride, coff, in_scales + k * sstride, soff);
-    for (int i0 = 0; i0 < K; i0 += PF) {
+        for (int k = 0; k < PF; ++k) src_load(buf[k], k);
+        int i0 = 0;
+        for (; i0 + 2 * PF <= K; i0 += PF) {
 #pragma unroll
-        for (int k = 0; k < PF; ++k) {
-            const int i = i0 + k;
-            if (i < K) {
+            for (int k = 0; k < PF; ++k) {
                 accumulate<EPL>(acc, buf[k]);
-                const int nx = i + PF;
-                if (nx < K)
-                    load_src<EPL>(buf[k], in_codes + (int64_t)nx * cstride, coff,
-                                  in_scales + (int64_t)nx * sstride, soff);
+                src_load(buf[k], i0 + PF + k);
             }
+        }
+#pragma unroll
+        for (int k = 0; k < PF; ++k) accumulate<EPL>(acc, buf[k]);
+        for (int i = i0 + PF; i < K; ++i) {          // fewer than PF left
+            SrcCodes<EPL> d;
+            src_load(d, i);
+            accumulate<EPL>(acc, d);
+        }
+    } else {
+        for (int i = 0; i < K; ++i) {
+            SrcCodes<EPL> d;
+            src_load(d, i);
+            accumulate<EPL>(acc, d);
         }
     }
     // |acc| as bit patterns: finite values order like unsigned integers and
@@ -490,8 +779,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
         for (int k = 0; k < EPL; ++k) acc[k] = 0.0f;
         for (int i = 0; i < K; ++i) {
             SrcCodes<EPL> d;
-            load_src<EPL>(d, in_codes + (int64_t)i * cstride, coff, in_scales + (int64_t)i * sstride,
-                          soff);
+            src_load(d, i);
             accumulate_direct<EPL>(acc, d);
         }
         mbits = 0;
@@ -501,13 +789,13 @@ __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
 
     if constexpr (OUT < 0) {
         const float a = __uint_as_float(group_max<G>(mbits));
-        BlockScale<7> bs(a);
+        BlockScale<7, false> bs(a);
         uint32_t q[EPL];
         bs.codes(acc, q);
         uint32_t packed[EPL / 8];
 #pragma unroll
         for (int k = 0; k < EPL / 8; ++k) packed[k] = pack_nibbles(q + 8 * k);
-        store_nibbles<EPL>(out_codes + e / 2, packed);
+        store_nibbles<EPL, ZPQ_NTS_REDUCE>(out_codes + e / 2, packed);
         if ((threadIdx.x & (G - 1)) == 0) out_scales[e / BLOCK] = bs.s;
     } else {
         // y = fl32(acc / divisor): div_cr is exact when the divisor is in
@@ -526,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
 #pragma unroll
             for (int k = 0; k < EPL; ++k) y[k] = acc[k] / divisor;
         }
-        store_out<OUT, EPL>(out_vals, e, y);
+        store_out<OUT, EPL, ZPQ_NTS_REDUCE>(out_vals, e, y);
     }
 }
 
@@ -557,29 +845,56 @@ inline unsigned grid_for(int64_t elems, int64_t per_wg) {
     return (unsigned)((elems + per_wg - 1) / per_wg);
 }
 
+// Compute units of the current device (cached per device id).
+inline int cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Launch grid for nvb virtual blocks: all of them, or a persistent grid of
+// per_cu workgroups per compute unit that loops over them.
+inline unsigned launch_grid(unsigned nvb, int per_cu) {
+    if (per_cu <= 0) return nvb;
+    const int64_t g = (int64_t)per_cu * cu_count();
+    return (unsigned)(g < (int64_t)nvb ? g : (int64_t)nvb);
+}
+
 // Launch shapes (elements per lane, tiles per lane, sources in flight).
-constexpr int kEplQuant = 16, kUQuant = 2;
-constexpr int kEplDequant = 16, kUDequant = 2;
-constexpr int kEplQgz = 16, kUQgz = 2;
-constexpr int kEplReduce = 16, kPfReduce = 4;
+// fp16/bf16 inputs use 8 elements per lane (one 16-byte load, so each load
+// instruction of a wave covers 1 KB contiguous) when the block fits in 32
+// lanes; fp32 inputs and block 512 use 16.
+template <int DT, int BLOCK, int EPL16>
+constexpr int epl_in() { return (DT != ZPQ_F32 && BLOCK / EPL16 <= 32) ? EPL16 : 16; }
+constexpr int kEplQuant = ZPQ_QUANT_EPL, kUQuant = ZPQ_QUANT_U;
+constexpr int kEplDequant = ZPQ_DEQUANT_EPL, kUDequant = ZPQ_DEQUANT_U;
+constexpr int kEplQgz = ZPQ_QGZ_EPL, kUQgz = ZPQ_QGZ_U;
+constexpr int kEplI4 = ZPQ_REDUCE_EPL_I4, kEplFl = ZPQ_REDUCE_EPL_FL;
+constexpr int kPfI4 = ZPQ_REDUCE_PF_I4, kPfFl = ZPQ_REDUCE_PF_FL;
+
+template <int DT, int BLOCK>
+void launch_quant_dt(const void* x, int64_t n, int8_t* codes, float* scales, hipStream_t st) {
+    constexpr int E = epl_in<DT, BLOCK, kEplQuant>();
+    const unsigned nvb = grid_for(n, (int64_t)kUQuant * kThreads * E);
+    hipLaunchKernelGGL((k_quant_i8<DT, BLOCK, E, kUQuant>), dim3(launch_grid(nvb, ZPQ_PERSIST_QUANT)),
+                       dim3(kThreads), 0, st, x, n, codes, scales, nvb);
+}
 
 template <int BLOCK>
 zpq_status launch_quant_i8(const void* x, int32_t dt, int64_t n, int8_t* codes, float* scales,
                            hipStream_t st) {
-    const unsigned grid = grid_for(n, (int64_t)kUQuant * kThreads * kEplQuant);
     switch (dt) {
-    case ZPQ_F32:
-        hipLaunchKernelGGL((k_quant_i8<ZPQ_F32, BLOCK, kEplQuant, kUQuant>), dim3(grid),
-                           dim3(kThreads), 0, st, x, n, codes, scales);
-        break;
-    case ZPQ_F16:
-        hipLaunchKernelGGL((k_quant_i8<ZPQ_F16, BLOCK, kEplQuant, kUQuant>), dim3(grid),
-                           dim3(kThreads), 0, st, x, n, codes, scales);
-        break;
-    default:
-        hipLaunchKernelGGL((k_quant_i8<ZPQ_BF16, BLOCK, kEplQuant, kUQuant>), dim3(grid),
-                           dim3(kThreads), 0, st, x, n, codes, scales);
-        break;
+    case ZPQ_F32: launch_quant_dt<ZPQ_F32, BLOCK>(x, n, codes, scales, st); break;
+    case ZPQ_F16: launch_quant_dt<ZPQ_F16, BLOCK>(x, n, codes, scales, st); break;
+    default: launch_quant_dt<ZPQ_BF16, BLOCK>(x, n, codes, scales, st); break;
     }
     return after_launch();
 }
@@ -587,72 +902,82 @@ zpq_status launch_quant_i8(const void* x, int32_t dt, int64_t n, int8_t* codes, 
 template <int BLOCK>
 zpq_status launch_dequant_i8(const int8_t* codes, const float* scales, int64_t n, void* y,
                              int32_t dt, hipStream_t st) {
-    const unsigned grid = grid_for(n, (int64_t)kUDequant * kThreads * kEplDequant);
+    constexpr int E = kEplDequant <= BLOCK ? kEplDequant : 16;
+    const unsigned nvb = grid_for(n, (int64_t)kUDequant * kThreads * E);
+    const unsigned grid = launch_grid(nvb, ZPQ_PERSIST_DEQUANT);
     switch (dt) {
     case ZPQ_F32:
-        hipLaunchKernelGGL((k_dequant_i8<ZPQ_F32, BLOCK, kEplDequant, kUDequant>), dim3(grid),
-                           dim3(kThreads), 0, st, codes, scales, n, y);
+        hipLaunchKernelGGL((k_dequant_i8<ZPQ_F32, BLOCK, E, kUDequant>), dim3(grid),
+                           dim3(kThreads), 0, st, codes, scales, n, y, nvb);
         break;
     case ZPQ_F16:
-        hipLaunchKernelGGL((k_dequant_i8<ZPQ_F16, BLOCK, kEplDequant, kUDequant>), dim3(grid),
-                           dim3(kThreads), 0, st, codes, scales, n, y);
+        hipLaunchKernelGGL((k_dequant_i8<ZPQ_F16, BLOCK, E, kUDequant>), dim3(grid),
+                           dim3(kThreads), 0, st, codes, scales, n, y, nvb);
         break;
     default:
-        hipLaunchKernelGGL((k_dequant_i8<ZPQ_BF16, BLOCK, kEplDequant, kUDequant>), dim3(grid),
-                           dim3(kThreads), 0, st, codes, scales, n, y);
+        hipLaunchKernelGGL((k_dequant_i8<ZPQ_BF16, BLOCK, E, kUDequant>), dim3(grid),
+                           dim3(kThreads), 0, st, codes, scales, n, y, nvb);
         break;
     }
+    return after_launch();
+}
+
+template <int DT, int BLOCK>
+zpq_status launch_qgz_dt(const void* g, int64_t n, int32_t L, int32_t N, uint8_t* codes,
+                         float* scales, hipStream_t st) {
+    constexpr int E = epl_in<DT, BLOCK, kEplQgz>();
+    const int64_t W = (int64_t)L * N;
+    const int64_t S = n / W;
+    const int64_t per_wg = (int64_t)kUQgz * kThreads * E;
+    const int64_t wps = (S + per_wg - 1) / per_wg;
+    if (wps * W > 0x7FFFFFFFLL) return ZPQ_ERR_SIZE;
+    const unsigned nvb = (unsigned)(wps * W);
+    hipLaunchKernelGGL((k_reorder_quant_i4<DT, BLOCK, E, kUQgz>),
+                       dim3(launch_grid(nvb, ZPQ_PERSIST_QGZ)), dim3(kThreads), 0, st, g, S, L, N,
+                       (uint32_t)wps, codes, scales, nvb);
     return after_launch();
 }
 
 template <int BLOCK>
 zpq_status launch_qgz_quant(const void* g, int32_t dt, int64_t n, int32_t L, int32_t N,
                             uint8_t* codes, float* scales, hipStream_t st) {
-    const int64_t W = (int64_t)L * N;
-    const int64_t S = n / W;
-    const int64_t per_wg = (int64_t)kUQgz * kThreads * kEplQgz;
-    const int64_t wps = (S + per_wg - 1) / per_wg;
-    if (wps * W > 0x7FFFFFFFLL) return ZPQ_ERR_SIZE;
-    const unsigned grid = (unsigned)(wps * W);
     switch (dt) {
-    case ZPQ_F32:
-        hipLaunchKernelGGL((k_reorder_quant_i4<ZPQ_F32, BLOCK, kEplQgz, kUQgz>), dim3(grid),
-                           dim3(kThreads), 0, st, g, S, L, N, (uint32_t)wps, codes, scales);
-        break;
-    case ZPQ_F16:
-        hipLaunchKernelGGL((k_reorder_quant_i4<ZPQ_F16, BLOCK, kEplQgz, kUQgz>), dim3(grid),
-                           dim3(kThreads), 0, st, g, S, L, N, (uint32_t)wps, codes, scales);
-        break;
-    default:
-        hipLaunchKernelGGL((k_reorder_quant_i4<ZPQ_BF16, BLOCK, kEplQgz, kUQgz>), dim3(grid),
-                           dim3(kThreads), 0, st, g, S, L, N, (uint32_t)wps, codes, scales);
-        break;
+    case ZPQ_F32: return launch_qgz_dt<ZPQ_F32, BLOCK>(g, n, L, N, codes, scales, st);
+    case ZPQ_F16: return launch_qgz_dt<ZPQ_F16, BLOCK>(g, n, L, N, codes, scales, st);
+    default: return launch_qgz_dt<ZPQ_BF16, BLOCK>(g, n, L, N, codes, scales, st);
     }
-    return after_launch();
 }
+
+template <int BLOCK, int EPL>
+constexpr int epl_for() { return EPL <= BLOCK ? EPL : BLOCK; }
 
 template <int BLOCK>
 zpq_status launch_reduce(const uint8_t* ic, const float* is, int32_t K, int64_t c, uint8_t* oc,
                          float* os, void* ov, int32_t odt, float divisor, hipStream_t st) {
-    const unsigned grid = grid_for(c, (int64_t)kThreads * kEplReduce);
+    constexpr int EI = epl_for<BLOCK, kEplI4>(), EF = epl_for<BLOCK, kEplFl>();
     const bool div_fast = divisor >= 1.0f && divisor <= 0x1p40f;
     const float rdiv = 1.0f / divisor;
     if (oc != nullptr) {
-        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, kEplReduce, -1, kPfReduce>), dim3(grid),
+        const unsigned nvb = grid_for(c, (int64_t)kThreads * EI);
+        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EI, -1, kPfI4>),
+                           dim3(launch_grid(nvb, ZPQ_PERSIST_REDUCE)), dim3(kThreads), 0, st, ic,
+                           is, K, c, oc, os, ov, divisor, rdiv, div_fast, nvb);
+        return after_launch();
+    }
+    const unsigned nvb = grid_for(c, (int64_t)kThreads * EF);
+    const dim3 grid(launch_grid(nvb, ZPQ_PERSIST_REDUCE));
+    if (odt == ZPQ_F32) {
+        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EF, ZPQ_F32, kPfFl>), grid,
                            dim3(kThreads), 0, st, ic, is, K, c, oc, os, ov, divisor, rdiv,
-                           div_fast);
-    } else if (odt == ZPQ_F32) {
-        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, kEplReduce, ZPQ_F32, kPfReduce>), dim3(grid),
-                           dim3(kThreads), 0, st, ic, is, K, c, oc, os, ov, divisor, rdiv,
-                           div_fast);
+                           div_fast, nvb);
     } else if (odt == ZPQ_F16) {
-        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, kEplReduce, ZPQ_F16, kPfReduce>), dim3(grid),
+        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EF, ZPQ_F16, kPfFl>), grid,
                            dim3(kThreads), 0, st, ic, is, K, c, oc, os, ov, divisor, rdiv,
-                           div_fast);
+                           div_fast, nvb);
     } else {
-        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, kEplReduce, ZPQ_BF16, kPfReduce>),
-                           dim3(grid), dim3(kThreads), 0, st, ic, is, K, c, oc, os, ov, divisor,
-                           rdiv, div_fast);
+        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EF, ZPQ_BF16, kPfFl>), grid,
+                           dim3(kThreads), 0, st, ic, is, K, c, oc, os, ov, divisor, rdiv,
+                           div_fast, nvb);
     }
     return after_launch();
 }

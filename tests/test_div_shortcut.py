@@ -1,0 +1,31 @@
+"""The GPU quantizer's division shortcut for 16-bit inputs, checked by
+exhaustion on the CPU (tests/div_check.c): for every positive finite fp16 or
+bf16 absmax a with s = fl32(a/qmax) >= 2^-100 and every value 0 <= x <= a of
+the same type, one residual correction of x * fl32(1/s) rounds to the same
+integer as the IEEE quotient fl32(x/s).  (fp32 inputs use two corrections,
+which Markstein's theorem makes exact without enumeration.)"""
+import os
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("div") / "div_check")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-pthread",
+                    os.path.join(HERE, "div_check.c"), "-o", exe, "-lm"], check=True)
+    return exe
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_one_correction_is_exact_for_16bit_inputs(checker, dtype, qmax):
+    threads = str(max(1, min(8, os.cpu_count() or 1)))
+    out = subprocess.run([checker, dtype, str(qmax), threads], check=True, capture_output=True,
+                         text=True).stdout.split()
+    assert out[0] == "mismatches" and int(out[1]) == 0, out
+    assert int(out[3]) > 5 * 10 ** 8          # about half of all (a, x) pairs, x >= 0

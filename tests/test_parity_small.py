@@ -207,3 +207,32 @@ def test_deterministic_repeat():
     b = zpq.qgz_reorder_quant_i4(g, 8, 48, 64)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_every_16bit_absmax(dtype):
+    """One block per positive finite fp16 / bf16 value a: [a, -a/3, a/7, 0, ...]
+    through the INT8 and the INT4 quantizer (scale, absmax code, a few
+    others) -- every scale the 16-bit inputs can produce."""
+    bits = np.arange(1, 0x7F80 if dtype == "bf16" else 0x7C00, dtype=np.uint32).astype(np.uint16)
+    a = oracle.bf16_to_f32(bits) if dtype == "bf16" else bits.view(np.float16).astype(np.float32)
+    B = 32
+    x32 = np.zeros((a.size, B), np.float32)
+    x32[:, 0] = a
+    x32[:, 1] = -a / 3
+    x32[:, 2] = a / 7
+    x32[:, 5] = a * 0.5
+    x = as_dtype(x32.ravel(), dtype)
+    if dtype == "bf16":
+        x.reshape(-1, B)[:, 0] = bits          # exact absmax bits
+    else:
+        x.view(np.uint16).reshape(-1, B)[:, 0] = bits
+    xd = to_device(x, dtype)
+    codes, scales = zpq.quant_i8(xd, B)
+    rc, rs = oracle.quant_i8(x, dtype, B)
+    assert_bits_equal(from_device(scales), rs, "INT8 scales")
+    assert_bits_equal(from_device(codes), rc, "INT8 codes")
+    c4, s4 = zpq.qgz_reorder_quant_i4(xd, 1, 1, B)
+    rc4, rs4 = oracle.qgz_reorder_quant_i4(x, dtype, 1, 1, B)
+    assert_bits_equal(from_device(s4), rs4, "INT4 scales")
+    assert_bits_equal(from_device(c4), rc4, "INT4 codes")
