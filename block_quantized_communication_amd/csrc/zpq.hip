@@ -690,6 +690,15 @@ __device__ __forceinline__ void accumulate(float (&acc)[EPL], const SrcCodes<EPL
     }
 }
 
+// max(m, |a|, |b|) in one v_max3_f32 with |.| source modifiers.  Written as
+// asm: the compiler would otherwise canonicalize each loop-carried operand
+// first (an extra instruction per element).
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+    float r;
+    asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(m));
+    return r;
+}
+
 template <int EPL>
 __device__ __forceinline__ void accumulate_direct(float (&acc)[EPL], const SrcCodes<EPL>& d) {
 #pragma unroll
@@ -768,12 +777,13 @@ __device__ __forceinline__ void reduce_tile(
             accumulate<EPL>(acc, d);
         }
     }
-    // |acc| as bit patterns: finite values order like unsigned integers and
-    // every inf / NaN pattern lies above FLT_MAX's
-    uint32_t mbits = 0;
+    // max |acc| (v_max3_f32 with |.| modifiers).  An overflowed -8s makes the
+    // lane's sums -inf, which this maximum exposes; a NaN sum would need a
+    // true partial sum that already overflowed (outside the domain).
+    float m = 0.0f;
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) mbits = max(mbits, __float_as_uint(acc[k]) & 0x7FFFFFFFu);
-    if (mbits > 0x7F7FFFFFu) {
+    for (int k = 0; k < EPL; k += 2) m = max3_abs(m, acc[k], acc[k + 1]);
+    if (!(m <= 3.4028234663852886e38f)) {
         // a non-finite sum: redo this lane with q * s directly
 #pragma unroll
         for (int k = 0; k < EPL; ++k) acc[k] = 0.0f;
@@ -782,10 +792,11 @@ __device__ __forceinline__ void reduce_tile(
             src_load(d, i);
             accumulate_direct<EPL>(acc, d);
         }
-        mbits = 0;
+        m = 0.0f;
 #pragma unroll
-        for (int k = 0; k < EPL; ++k) mbits = max(mbits, __float_as_uint(acc[k]) & 0x7FFFFFFFu);
+        for (int k = 0; k < EPL; k += 2) m = max3_abs(m, acc[k], acc[k + 1]);
     }
+    const uint32_t mbits = __float_as_uint(m);
 
     if constexpr (OUT < 0) {
         const float a = __uint_as_float(group_max<G>(mbits));
@@ -802,7 +813,7 @@ __device__ __forceinline__ void reduce_tile(
         // [1, 2^40] (checked on the host: the quotient cannot overflow) and
         // |acc| >= 2^-60 or acc == 0 (the quotient is normal and no residual
         // underflows); otherwise the IEEE operator.
-        bool fast = div_fast && mbits <= 0x7F7FFFFFu;
+        bool fast = div_fast && m <= 3.4028234663852886e38f;
 #pragma unroll
         for (int k = 0; k < EPL; ++k)
             fast = fast && (fabsf(acc[k]) >= 0x1p-60f || acc[k] == 0.0f);
