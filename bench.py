@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.5)
+    ap.add_argument("--study", choices=["hop-count", "blocking"], default=None,
+                    help="run an error study instead of the throughput benchmark")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 1 GiB with torch (a plain copy kernel of known "
                          "size, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -61,6 +63,13 @@ def main():
 
     import block_quantized_communication_amd as zpq
     import synth
+
+    if args.study == "hop-count":
+        print(json.dumps(hop_count_study(np, torch, zpq, synth)), flush=True)
+        return
+    if args.study == "blocking":
+        print(json.dumps(blocking_study(np, torch, zpq, synth)), flush=True)
+        return
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
@@ -269,6 +278,120 @@ def verify(zpq, synth, np, torch, layer_h, grad_h, gath_codes, gath_scales, y_la
     s1g = send1_c.cpu().numpy()
     ok &= np.array_equal(np.concatenate([s1g[p // 2:p // 2 + B // 2] for p in pos]), c1)
     return {"sampled_blocks": int(bl.size + pos.size + ob.size), "bit_exact": bool(ok)}
+
+
+def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):
+    """Error of INT4 gradient averaging against the exact mean, as the world
+    size W grows: qgZ's two hops (L = min(W, 8) local ranks, N = W/L nodes:
+    every value is quantized twice) against a compressed ring reduce-scatter
+    (the running partial sum is requantized at each of the W - 1 hops).  One
+    slice of S elements per rank, gradients N(0, 1e-3) with a per-block
+    variance multiplier 10^U(-2, 2) (the qgZ hop-1 workload's law), INT4 with
+    block B, all steps on the GPU kernels.  The claim being measured: error
+    that compounds with the hop count is why the pages replace reduce-scatter
+    by an all-to-all (LIT-102 anthology record, Key takeaways)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = []
+    for W in (2, 4, 8, 16, 32, 64, 128, 384):
+        g = np.stack([synth.blockvar_normal(seed, 1000 + r, S, B, 1e-3, -2.0, 2.0)
+                      for r in range(W)])                               # [W][S] fp32
+        exact = g.astype(np.float64).mean(axis=0)
+        gd = torch.from_numpy(g).to(dev)
+        # every rank's slice quantized once (the send-side kernel, L = N = 1)
+        q = [zpq.qgz_reorder_quant_i4(gd[r], 1, 1, B) for r in range(W)]
+        # compressed ring: partial = requant(dequant(partial) + dequant(own)), W - 1 hops
+        pc, ps = q[0]
+        for r in range(1, W):
+            cc = torch.cat([pc, q[r][0]])
+            sc = torch.cat([ps, q[r][1]])
+            pc, ps = zpq.qgz_dequant_reduce_requant_i4(cc, sc, 2, S, B)
+        ring = zpq.qgz_dequant_reduce_requant_i4(pc, ps, 1, S, B, out_dtype=torch.float32,
+                                                 divisor=float(W))
+        # qgZ: hop 1 over L local ranks (requantize), hop 2 over N nodes (average)
+        L = min(W, 8)
+        N = W // L
+        hop1 = []
+        for m in range(N):
+            cc = torch.cat([q[m * L + i][0] for i in range(L)])
+            sc = torch.cat([q[m * L + i][1] for i in range(L)])
+            hop1.append(zpq.qgz_dequant_reduce_requant_i4(cc, sc, L, S, B))
+        cc = torch.cat([h[0] for h in hop1])
+        sc = torch.cat([h[1] for h in hop1])
+        qgz = zpq.qgz_dequant_reduce_requant_i4(cc, sc, N, S, B, out_dtype=torch.float32,
+                                                divisor=float(W))
+        torch.cuda.synchronize()
+        scale = float(np.sqrt(np.mean(exact ** 2)))
+
+        def err(y):
+            d = y.cpu().numpy().astype(np.float64) - exact
+            return round(float(np.sqrt(np.mean(d ** 2)) / scale), 5)
+        rows.append({"W": W, "L": L, "N": N, "quantizations_qgz": 2,
+                     "quantizations_ring": W, "rel_rms_err_qgz": err(qgz),
+                     "rel_rms_err_ring": err(ring)})
+        print(f"[study] W={W}: qgZ {rows[-1]['rel_rms_err_qgz']}, ring "
+              f"{rows[-1]['rel_rms_err_ring']}", file=sys.stderr, flush=True)
+    return {"study": "hop-count error: qgZ two-hop all-to-all vs compressed ring "
+                     "reduce-scatter (INT4, block 128)", "slice_elems": S, "rows": rows,
+            "error": "RMS(y - exact mean) / RMS(exact mean), fp64 reference"}
+
+
+def blocking_study(np, torch, zpq, synth, reps=20):
+    """INT8 weight quantization with one scale per tensor against one scale
+    per block (the summary page's ablation: non-blocked quantization of the
+    weights hurt, block-based did not).  Reconstruction error of both on the
+    outlier tensor (fp16 N(0, 0.02) with 0.1% N(0, 1) outliers) and on the
+    layer shard (fp16 N(0, 0.02)); kernel throughput of both on the shard.
+    The GPU kernels quantize and dequantize; the error is taken in fp64."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cases = {"outliers_2^20": synth.qwz_roundtrip(), "layer_shard": synth.qwz_shard(0)}
+    rows = []
+    for name, x in cases.items():
+        xd = torch.from_numpy(x).to(dev)
+        ref = x.astype(np.float64)
+        scale = float(np.sqrt(np.mean(ref ** 2)))
+
+        def err(y):
+            d = y.cpu().numpy().astype(np.float64) - ref
+            return {"rel_rms_err": round(float(np.sqrt(np.mean(d ** 2)) / scale), 6),
+                    "max_abs_err": float(np.abs(d).max())}
+        c, s1 = zpq.quant_i8_tensor(xd)
+        r = {"tensor": name, "n": int(x.size),
+             # the one scale repeated per 256-block: the same products fl32(q * s)
+             "per_tensor": err(zpq.dequant_i8(c, s1.expand(x.size // 256).contiguous(), 256,
+                                              torch.float16))}
+        for B in (32, 64, 128, 256, 512):
+            c, s = zpq.quant_i8(xd, B)
+            r[f"block_{B}"] = err(zpq.dequant_i8(c, s, B, torch.float16))
+        rows.append(r)
+        print(f"[study] {name}: per-tensor {r['per_tensor']['rel_rms_err']}, block 256 "
+              f"{r['block_256']['rel_rms_err']}", file=sys.stderr, flush=True)
+    x = torch.from_numpy(cases["layer_shard"]).to(dev)
+    n = x.numel()
+    codes = torch.empty(n, dtype=torch.int8, device=dev)
+    sc = torch.empty(n // 256, dtype=torch.float32, device=dev)
+    s1 = torch.empty(1, dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream()
+    timing = {}
+    for label, fn, nbytes in (
+            ("block_256", lambda: zpq.quant_i8(x, 256, out=(codes, sc), stream=st), 3 * n + n // 64),
+            ("per_tensor", lambda: zpq.quant_i8_tensor(x, out=(codes, s1), stream=st), 3 * n)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        timing[label] = {"us_per_call": round(us, 2),
+                         "effective_GBps": round(nbytes / us / 1e3, 1)}
+    return {"study": "INT8 weight quantization: per-tensor scale vs per-block scales",
+            "rows": rows, "quantize_timing_layer_shard": timing,
+            "effective_bytes": "2n read + n codes written (+ scales), whatever the passes",
+            "error": "RMS(dequant(quant(x)) - x) / RMS(x) in fp64; max |error|"}
 
 
 def cpu_baseline(np, layer_h, grad_h, frac):

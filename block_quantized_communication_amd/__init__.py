@@ -28,7 +28,7 @@ STATUS = {0: "ok", 1: "null pointer", 2: "bad size", 3: "bad block", 4: "misalig
           5: "bad dtype", 6: "bad output mode", 7: "launch failed", 8: "bad argument",
           9: "output overlaps input"}
 
-EXPORTS = ("zpq_quant_i8", "zpq_dequant_i8", "zpq_qgz_reorder_quant_i4",
+EXPORTS = ("zpq_quant_i8", "zpq_dequant_i8", "zpq_quant_i8_tensor", "zpq_qgz_reorder_quant_i4",
            "zpq_qgz_dequant_reduce_requant_i4", "zpq_status_str", "zpq_abi_version")
 
 
@@ -52,6 +52,7 @@ def lib():
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.zpq_quant_i8.argtypes = [vp, i32, i64, i32, vp, vp, vp]
         L.zpq_dequant_i8.argtypes = [vp, vp, i64, i32, vp, i32, vp]
+        L.zpq_quant_i8_tensor.argtypes = [vp, i32, i64, vp, vp, vp]
         L.zpq_qgz_reorder_quant_i4.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp]
         L.zpq_qgz_dequant_reduce_requant_i4.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32,
                                                         f32, vp]
@@ -125,6 +126,24 @@ def quant_i8(x, block=256, out=None, stream=None):
                             _stream(stream))
     _check(rc, "zpq_quant_i8")
     return codes, scales
+
+
+def quant_i8_tensor(x, out=None, stream=None):
+    """Non-blocked INT8 quantization, one scale for all of x -> (codes, scale[1])."""
+    torch = _torch()
+    n = x.numel()
+    if out is None:
+        out = (torch.empty(n, dtype=torch.int8, device=x.device),
+               torch.empty(1, dtype=torch.float32, device=x.device))
+    codes, scale = out
+    _need(codes, torch.int8, n, "codes")
+    _need(scale, torch.float32, 1, "scale")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    rc = lib().zpq_quant_i8_tensor(_ptr(x), dtype_code(x.dtype), n, _ptr(codes), _ptr(scale),
+                                   _stream(stream))
+    _check(rc, "zpq_quant_i8_tensor")
+    return codes, scale
 
 
 def dequant_i8(codes, scales, block=256, dtype=None, out=None, stream=None):

@@ -470,6 +470,85 @@ __global__ __launch_bounds__(kThreads) void k_quant_i8(const void* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Per-tensor INT8 quantization (non-blocked ablation): three passes.
+//  1. every workgroup writes the bit pattern of its max |x| into slot vb of a
+//     uint32 array that overlays the codes buffer (overwritten in pass 3);
+//  2. one workgroup reduces those maxima and writes s = fl32(a/127);
+//  3. the codes, with that one scale (the block quantizer's code path).
+constexpr int kTensorEpl = 8, kTensorU = 2;
+constexpr int64_t kTensorTile = (int64_t)kTensorU * kThreads * kTensorEpl;
+
+// max over a workgroup of per-lane values (bit patterns of non-negative floats)
+__device__ __forceinline__ uint32_t workgroup_max(uint32_t v) {
+    __shared__ uint32_t part[kThreads / 64];
+    v = group_max<32>(v);
+    v = max(v, (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+    v = max(v, (uint32_t)__builtin_amdgcn_readlane((int)v, 0));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) m = max(m, part[i]);
+    return m;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_tensor_absmax(const void* __restrict__ x, int64_t n,
+                                                            uint32_t* __restrict__ partial) {
+    const int64_t base = (int64_t)blockIdx.x * kTensorTile;
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < kTensorU; ++u) {
+        const int64_t e = base + (int64_t)u * (kThreads * kTensorEpl) + threadIdx.x * kTensorEpl;
+        if (e < n) {
+            InTile<DT, kTensorEpl> t;
+            t.template load<true>(x, e);
+            m = max(m, t.absmax_bits());
+        }
+    }
+    m = workgroup_max(m);
+    if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(kThreads) void k_tensor_scale(const uint32_t* __restrict__ partial,
+                                                           int64_t count, float* __restrict__ scale) {
+    uint32_t m = 0;
+    for (int64_t i = threadIdx.x; i < count; i += kThreads) m = max(m, partial[i]);
+    m = workgroup_max(m);
+    if (threadIdx.x == 0) scale[0] = __uint_as_float(m) / 127.0f;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_tensor_codes(const void* __restrict__ x, int64_t n,
+                                                           const float* __restrict__ scale,
+                                                           int8_t* __restrict__ codes) {
+    constexpr int EPL = kTensorEpl;
+    const float s = scale[0];
+    const bool fast = s >= 0x1p-100f;
+    const BlockScale<127, DT != ZPQ_F32> bs(s, fast ? 1.0f / s : 0.0f);
+    const int64_t base = (int64_t)blockIdx.x * kTensorTile;
+    InTile<DT, EPL> tile[kTensorU];
+#pragma unroll
+    for (int u = 0; u < kTensorU; ++u) {
+        const int64_t e = base + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
+        if (e < n) tile[u].template load<true>(x, e); else tile[u].zero();
+    }
+#pragma unroll
+    for (int u = 0; u < kTensorU; ++u) {
+        const int64_t e = base + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
+        float v[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) v[k] = tile[u].get(k);
+        uint32_t q[EPL];
+        bs.codes(v, q);
+        if (e < n)
+            st_stream<false>(u32x2{pack_low_bytes(q[0], q[1], q[2], q[3]),
+                                   pack_low_bytes(q[4], q[5], q[6], q[7])},
+                             reinterpret_cast<u32x2*>(codes + e));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // K2: qwZ INT8 dequantize into fp32 / fp16 / bf16.
 template <int OT, int EPL, bool NT>
 __device__ __forceinline__ void store_out(void* __restrict__ y, int64_t e, const float (&v)[EPL]) {
@@ -1021,6 +1100,57 @@ zpq_status zpq_quant_i8(const void* x, int32_t x_dtype, int64_t n, int32_t block
         return ZPQ_ERR_ALIAS;
     hipStream_t st = static_cast<hipStream_t>(stream);
     ZPQ_DISPATCH_BLOCK(block, launch_quant_i8, (x, x_dtype, n, codes, scales, st))
+}
+
+zpq_status zpq_quant_i8_tensor(const void* x, int32_t x_dtype, int64_t n, int8_t* codes,
+                               float* scale, zpq_stream stream) {
+    if (n < 0 || n % 16 != 0) return ZPQ_ERR_SIZE;
+    const int64_t eb = dtype_bytes(x_dtype);
+    if (eb == 0) return ZPQ_ERR_DTYPE;
+    if (!scale) return ZPQ_ERR_NULL;
+    if (n > 0 && (!x || !codes)) return ZPQ_ERR_NULL;
+    if (!aligned16(scale) || (n > 0 && (!aligned16(x) || !aligned16(codes)))) return ZPQ_ERR_ALIGN;
+    if (overlaps(x, n * eb, codes, n) || overlaps(x, n * eb, scale, 4) ||
+        overlaps(codes, n, scale, 4))
+        return ZPQ_ERR_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t nwg = (n + kTensorTile - 1) / kTensorTile;
+    if (nwg > 0x7FFFFFFFLL) return ZPQ_ERR_SIZE;
+    uint32_t* partial = reinterpret_cast<uint32_t*>(codes);     // nwg * 4 <= n bytes
+    if (nwg > 0) {
+        switch (x_dtype) {
+        case ZPQ_F32:
+            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_F32>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
+                               x, n, partial);
+            break;
+        case ZPQ_F16:
+            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_F16>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
+                               x, n, partial);
+            break;
+        default:
+            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_BF16>, dim3((unsigned)nwg), dim3(kThreads), 0,
+                               st, x, n, partial);
+            break;
+        }
+    }
+    hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(kThreads), 0, st, partial, nwg, scale);
+    if (nwg > 0) {
+        switch (x_dtype) {
+        case ZPQ_F32:
+            hipLaunchKernelGGL(k_tensor_codes<ZPQ_F32>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
+                               x, n, scale, codes);
+            break;
+        case ZPQ_F16:
+            hipLaunchKernelGGL(k_tensor_codes<ZPQ_F16>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
+                               x, n, scale, codes);
+            break;
+        default:
+            hipLaunchKernelGGL(k_tensor_codes<ZPQ_BF16>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
+                               x, n, scale, codes);
+            break;
+        }
+    }
+    return after_launch();
 }
 
 zpq_status zpq_dequant_i8(const int8_t* codes, const float* scales, int64_t n, int32_t block,

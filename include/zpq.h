@@ -88,6 +88,21 @@ zpq_status zpq_dequant_i8(const int8_t* codes, const float* scales, int64_t n,
                           int32_t block, void* y, int32_t y_dtype, zpq_stream stream);
 
 /*
+ * Non-blocked (per-tensor) INT8 quantization: one scale for the whole tensor.
+ * The ablation baseline of qwZ ([SUM] Measured effects table: basic
+ * non-blocked instead of block-based quantization, which hurt convergence;
+ * Surprising findings: naive non-blocked INT8 weights diverged).
+ *
+ *   x      [n] elements of type x_dtype; n % 16 == 0 (callers pad with zeros)
+ *   codes  [n] int8 codes in [-127, 127]                          (written)
+ *   scale  [1] fp32: fl32(max|x| / 127)                            (written)
+ * The codes buffer also holds intermediate per-workgroup maxima during the
+ * call (three kernels on `stream`); nothing else is touched.
+ */
+zpq_status zpq_quant_i8_tensor(const void* x, int32_t x_dtype, int64_t n, int8_t* codes,
+                               float* scale, zpq_stream stream);
+
+/*
  * qgZ, before the intra-node all-to-all: tensor-slice reordering fused with
  * INT4 block quantization ([SUM] "Approach": slice reordering for correct
  * placement ahead of a 2-hop all-to-all of INT4 gradients; [ABS]: all-to-all

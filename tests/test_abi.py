@@ -77,6 +77,23 @@ def test_dequant_i8_validation():
     assert dq8(n=0, codes=0, scales=0, y=0) == OK
 
 
+def qt8(x=P, dt=2, n=1024, codes=P + (1 << 16), scale=P + (1 << 18)):
+    return zpq.lib().zpq_quant_i8_tensor(vp(x), dt, n, vp(codes), vp(scale), NUL)
+
+
+def test_quant_i8_tensor_validation():
+    assert qt8(n=1000) == SIZE
+    assert qt8(n=-16) == SIZE
+    assert qt8(dt=5) == DTYPE
+    assert qt8(scale=0) == NULL
+    assert qt8(x=0) == NULL
+    assert qt8(codes=0) == NULL
+    assert qt8(x=P + 4) == ALIGN
+    assert qt8(scale=P + (1 << 18) + 4) == ALIGN
+    assert qt8(codes=P + 256) == ALIAS           # codes inside x's 2 KB
+    assert qt8(scale=P + (1 << 16) + 64) == ALIAS
+
+
 def rq4(g=P, dt=2, n=8 * 4 * 128 * 3, L=8, N=4, block=128, codes=P + (1 << 18),
         scales=P + (1 << 19)):
     return zpq.lib().zpq_qgz_reorder_quant_i4(vp(g), dt, n, L, N, block, vp(codes), vp(scales),

@@ -236,3 +236,51 @@ def test_every_16bit_absmax(dtype):
     rc4, rs4 = oracle.qgz_reorder_quant_i4(x, dtype, 1, 1, B)
     assert_bits_equal(from_device(s4), rs4, "INT4 scales")
     assert_bits_equal(from_device(c4), rc4, "INT4 codes")
+
+
+def test_ring_reduce_scatter_chain_matches_oracle():
+    """The compressed-ring chain of the hop-count study (K = 2 requantization
+    per hop, 15 hops) on the GPU equals the oracle's chain bit for bit."""
+    import synth
+    S, B, W = 4096, 128, 16
+    g = np.stack([synth.blockvar_normal(40, 1000 + r, S, B, 1e-3, -2.0, 2.0) for r in range(W)])
+    qg = [zpq.qgz_reorder_quant_i4(to_device(g[r]), 1, 1, B) for r in range(W)]
+    qo = [oracle.qgz_reorder_quant_i4(g[r], "f32", 1, 1, B) for r in range(W)]
+    pc, ps = qg[0]
+    oc, os_ = qo[0]
+    import torch
+    for r in range(1, W):
+        pc, ps = zpq.qgz_dequant_reduce_requant_i4(torch.cat([pc, qg[r][0]]),
+                                                   torch.cat([ps, qg[r][1]]), 2, S, B)
+        oc, os_ = oracle.qgz_dequant_reduce_requant_i4(np.concatenate([oc, qo[r][0]]),
+                                                       np.concatenate([os_, qo[r][1]]), 2, S, B)
+    assert_bits_equal(from_device(pc), oc, "ring codes")
+    assert_bits_equal(from_device(ps), os_, "ring scales")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("kind", ["outliers", "adversarial", "tiny", "zero", "max_last"])
+def test_quant_i8_tensor(dtype, kind):
+    """Per-tensor INT8 quantization equals the oracle's block quantizer with
+    one block spanning the tensor, for one to several hundred workgroups."""
+    rng = np.random.default_rng(len(kind) * 3 + len(dtype))
+    for n in (16, 3 * 4096 + 16, (1 << 18) + 48, 3 << 20):
+        if kind == "outliers":
+            x = (rng.standard_normal(n) * 0.02).astype(np.float32)
+            pos = rng.integers(0, n, max(1, n // 1000))
+            x[pos] = rng.standard_normal(pos.size).astype(np.float32)
+        elif kind == "adversarial":
+            x = adversarial_f32(rng, n, 16)
+        elif kind == "tiny":                  # scale below 2^-100 (f32) / subnormal inputs
+            x = (rng.standard_normal(n) * 1e-40).astype(np.float32)
+        elif kind == "zero":
+            x = np.zeros(n, np.float32)
+        else:                                  # the tensor's max in its very last element
+            x = rng.uniform(-1, 1, n).astype(np.float32)
+            x[-1] = -3.0
+        xs = as_dtype(x, dtype)
+        print(f"quant_i8_tensor dtype={dtype} kind={kind} n={n}", flush=True)
+        codes, scale = zpq.quant_i8_tensor(to_device(xs, dtype))
+        rc, rs = oracle.quant_i8(xs, dtype, n)
+        assert_bits_equal(from_device(scale), rs, "scale")
+        assert_bits_equal(from_device(codes), rc, "codes")
