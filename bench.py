@@ -35,8 +35,13 @@ METRIC = "effective HBM GB/s per kernel and % of MI355X peak (qwZ quant/dequant,
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="before the warm-up steps, run untimed steps for this long: under "
+                         "sustained HBM load the chip's power controller lowers the clocks and "
+                         "takes tens of ms to settle, and the timed steps should see the settled "
+                         "state")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.5)
@@ -145,6 +150,13 @@ def main():
             if events is not None:
                 events[i][1].record()
 
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -210,6 +222,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -51,7 +51,7 @@
 #define ZPQ_QGZ_EPL 8          // elements per lane, reorder + INT4 quantize of fp16/bf16
 #endif
 #ifndef ZPQ_QGZ_U
-#define ZPQ_QGZ_U 4            // tiles per lane, reorder + INT4 quantize
+#define ZPQ_QGZ_U 2            // tiles per lane, reorder + INT4 quantize
 #endif
 #ifndef ZPQ_REDUCE_EPL_I4
 #define ZPQ_REDUCE_EPL_I4 16   // elements per lane, hop-1 receive (INT4 out)
@@ -195,110 +195,69 @@ __device__ __forceinline__ uint32_t round_code_fast(float t) {
     return __float_as_uint(t + 12582912.0f);
 }
 
-// Per-block quantizer state: scale s = fl32(a / QMAX) and, when
-// s >= 2^-100, its correctly rounded reciprocal for the division above.
-// The scale uses the corrected division by the constant QMAX (exact for
-// a >= 2^-90, where no residual underflows), else the IEEE operator.
-// ONE_STEP selects div_1c for the codes (16-bit inputs only).
+// Codes of N values given the final scale s.  Fast path (s >= 2^-100):
+// ONE_STEP (16-bit inputs) takes one residual correction with any r within
+// one ulp of 1/s; otherwise two corrections with r = fl32(1/s).  The slow
+// path (tiny or zero scale, block-uniform) divides with the IEEE operator.
+template <int QMAX, bool ONE_STEP, int N>
+__device__ __forceinline__ void codes_of(float s, float r, bool fast, const float (&v)[N],
+                                         uint32_t (&out)[N]) {
+    if (fast) {
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            out[k] = round_code_fast(ONE_STEP ? div_1c(v[k], s, r) : div_cr(v[k], s, r));
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) out[k] = round_code<QMAX>(s != 0.0f ? v[k] / s : 0.0f);
+    }
+}
+
+// Per-block quantizer state from the block absmax a: scale s = fl32(a / QMAX)
+// and, on the fast path, a reciprocal r.
+//  * fp32 inputs (ONE_STEP false): s by the corrected division by the
+//    constant QMAX (exact for a >= 2^-90, where no residual underflows), else
+//    the IEEE operator; fast when s >= 2^-100, with r = fl32(1/s).
+//  * 16-bit inputs (ONE_STEP true), branch-free: s = fl32(a * k) plus one
+//    residual correction (k = fl32(1/QMAX)), and r = the hardware reciprocal
+//    of s refined by one Newton step, which leaves r within one ulp of 1/s.
+//    For every fp16 and bf16 absmax a >= 2^-90 that s is exactly
+//    fl32(a / QMAX), and div_1c with either float next to 1/s gives the IEEE
+//    codes: both checked by exhaustion over all (a, x) pairs of both types
+//    and both QMAX.  fast = (a >= 2^-90); a slower block's exact scale
+//    a / QMAX (possibly subnormal) is computed by codes(), on its slow path.
 template <int QMAX, bool ONE_STEP>
 struct BlockScale {
-    float s, r;
+    float a, s, r;
     bool fast;
     BlockScale() = default;
-    // From a precomputed (s, fl32(1/s)) pair; r == 0 marks the slow path.
-    __device__ __forceinline__ BlockScale(float s_, float r_) : s(s_), r(r_), fast(r_ != 0.0f) {}
-    __device__ __forceinline__ explicit BlockScale(float a) {
+    __device__ __forceinline__ explicit BlockScale(float a_) : a(a_) {
+        constexpr float kQ = (float)QMAX;
         constexpr float kInvQ = 1.0f / (float)QMAX;      // fl32(1/QMAX), folded by the compiler
-        if (a >= 0x1p-90f) s = div_cr(a, (float)QMAX, kInvQ);
-        else s = a / (float)QMAX;
-        fast = s >= 0x1p-100f;
-        r = fast ? 1.0f / s : 0.0f;
-    }
-    // Codes of N values (as rounded bit patterns).  The slow path (tiny or
-    // zero scale, block-uniform) divides with the IEEE operator.
-    template <int N>
-    __device__ __forceinline__ void codes(const float (&v)[N], uint32_t (&out)[N]) const {
-        if (fast) {
-#pragma unroll
-            for (int k = 0; k < N; ++k)
-                out[k] = round_code_fast(ONE_STEP ? div_1c(v[k], s, r) : div_cr(v[k], s, r));
+        if constexpr (ONE_STEP) {
+            const float s0 = a * kInvQ;
+            s = __builtin_fmaf(__builtin_fmaf(-s0, kQ, a), kInvQ, s0);
+            const float r0 = __builtin_amdgcn_rcpf(s);
+            r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+            fast = a >= 0x1p-90f;
         } else {
-#pragma unroll
-            for (int k = 0; k < N; ++k) out[k] = round_code<QMAX>(s != 0.0f ? v[k] / s : 0.0f);
+            if (a >= 0x1p-90f) s = div_cr(a, kQ, kInvQ);
+            else s = a / kQ;
+            fast = s >= 0x1p-100f;
+            r = fast ? 1.0f / s : 0.0f;
+        }
+    }
+    // Codes of N values (as rounded bit patterns); afterwards s is the
+    // block's scale on every path.
+    template <int N>
+    __device__ __forceinline__ void codes(const float (&v)[N], uint32_t (&out)[N]) {
+        if (fast) {
+            codes_of<QMAX, ONE_STEP>(s, r, true, v, out);
+        } else {
+            if constexpr (ONE_STEP) s = a / (float)QMAX;
+            codes_of<QMAX, ONE_STEP>(s, r, false, v, out);
         }
     }
 };
-
-// ---------------------------------------------------------------------------
-// Scale tables for 16-bit inputs.  The block absmax a of fp16 or bf16 data is
-// a 16-bit value m * 2^k (m its integer significand).  While a/QMAX and its
-// reciprocal stay normal floats, fl32(a/QMAX) = fl32(m/QMAX) * 2^k and
-// fl32(1/s) = fl32(1/fl32(m/QMAX)) * 2^-k exactly, so a table indexed by the
-// significand (folded at compile time: the compiler evaluates the IEEE
-// divisions) plus two exact v_ldexp_f32 give s and 1/s.  The tables are small
-// (fp16: 2048 entries, bf16: 128) so lookups hit in the per-CU cache.
-struct ScaleRecip {
-    float s, r;
-};
-
-template <int QMAX, int N, int LEAD>
-struct MantTable {
-    ScaleRecip e[N];
-};
-
-// entry i: significand LEAD + i for i < N1, else (fp16 subnormals) i - N1
-template <int QMAX, int N, int LEAD, int N1>
-constexpr MantTable<QMAX, N, LEAD> make_mant_table() {
-    MantTable<QMAX, N, LEAD> t{};
-    for (int i = 0; i < N; ++i) {
-        const float m = i < N1 ? (float)(LEAD + i) : (float)(i - N1);
-        const float sc = m / (float)QMAX;
-        t.e[i].s = sc;
-        t.e[i].r = sc != 0.0f ? 1.0f / sc : 0.0f;
-    }
-    return t;
-}
-
-// fp16: normal a = (1024 + M) * 2^(E-25); subnormal a = M * 2^-24
-__device__ constexpr MantTable<127, 2048, 1024> kF16Q127 = make_mant_table<127, 2048, 1024, 1024>();
-__device__ constexpr MantTable<7, 2048, 1024> kF16Q7 = make_mant_table<7, 2048, 1024, 1024>();
-// bf16: normal a = (128 + M) * 2^(E-134)
-__device__ constexpr MantTable<127, 128, 128> kBF16Q127 = make_mant_table<127, 128, 128, 128>();
-__device__ constexpr MantTable<7, 128, 128> kBF16Q7 = make_mant_table<7, 128, 128, 128>();
-
-template <int DT, int QMAX>
-__device__ __forceinline__ const ScaleRecip* mant_table() {
-    if constexpr (DT == ZPQ_F16) return QMAX == 127 ? kF16Q127.e : kF16Q7.e;
-    else return QMAX == 127 ? kBF16Q127.e : kBF16Q7.e;
-}
-
-// (s, 1/s) of a 16-bit absmax pattern h (sign cleared); r == 0 when the block
-// needs the slow path, and then s is exact (IEEE division) or 0 for a
-// non-finite absmax (outside the domain).
-template <int DT, int QMAX>
-__device__ __forceinline__ ScaleRecip scale_of16(uint32_t h) {
-    ScaleRecip out;
-    if constexpr (DT == ZPQ_F16) {
-        const uint32_t E = h >> 10, M = h & 0x3FFu;
-        const ScaleRecip t = mant_table<DT, QMAX>()[E ? M : 1024u + M];
-        const int k = E ? (int)E - 25 : -24;        // fp16 scales are always normal
-        out.s = __builtin_amdgcn_ldexpf(t.s, k);
-        out.r = __builtin_amdgcn_ldexpf(t.r, -k);
-        if (E == 31) out.s = out.r = 0.0f;
-    } else {
-        const uint32_t E = h >> 7, M = h & 0x7Fu;
-        const ScaleRecip t = mant_table<DT, QMAX>()[M];
-        const int k = (int)E - 134;
-        out.s = __builtin_amdgcn_ldexpf(t.s, k);
-        out.r = __builtin_amdgcn_ldexpf(t.r, -k);
-        if (!(out.s >= 0x1p-100f) || E == 0 || E == 255) {
-            // tiny or non-finite absmax: exact scale, slow path
-            out.s = E == 255 ? 0.0f : __uint_as_float(h << 16) / (float)QMAX;
-            out.r = 0.0f;
-        }
-    }
-    return out;
-}
 
 // ---------------------------------------------------------------------------
 // Byte packing with v_perm_b32.  perm(a, b, sel): selector byte 0..3 picks a
@@ -369,28 +328,11 @@ struct InTile {
             return __uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
         }
     }
-    // 15-bit magnitude pattern of max |x| over the tile (16-bit types only)
-    __device__ __forceinline__ uint32_t absmax16() const {
-        static_assert(DT != ZPQ_F32, "16-bit inputs");
-        u16x2 m = {0, 0};
-#pragma unroll
-        for (int i = 0; i < WORDS; ++i) {
-            const uint32_t a = w[i] & 0x7FFF7FFFu;
-            const u16x2 v = {(unsigned short)(a & 0xFFFFu), (unsigned short)(a >> 16)};
-            m = __builtin_elementwise_max(m, v);
-        }
-        return m.x > m.y ? m.x : m.y;
-    }
     // The block's quantizer state; every lane of the aligned group of G lanes
     // holding the block gets the same one.
     template <int QMAX, int G>
     __device__ __forceinline__ BlockScale<QMAX, DT != ZPQ_F32> block_scale() const {
-        if constexpr (DT == ZPQ_F32) {
-            return BlockScale<QMAX, false>(__uint_as_float(group_max<G>(absmax_bits())));
-        } else {
-            const ScaleRecip sr = scale_of16<DT, QMAX>(group_max<G>(absmax16()));
-            return BlockScale<QMAX, true>(sr.s, sr.r);
-        }
+        return BlockScale<QMAX, DT != ZPQ_F32>(__uint_as_float(group_max<G>(absmax_bits())));
     }
     // bit pattern of max |x| over the tile, as fp32
     __device__ __forceinline__ uint32_t absmax_bits() const {
@@ -404,11 +346,8 @@ struct InTile {
             // two elements per v_pk_max_u16
             u16x2 m = {0, 0};
 #pragma unroll
-            for (int i = 0; i < WORDS; ++i) {
-                uint32_t a = w[i] & 0x7FFF7FFFu;
-                u16x2 v = {(unsigned short)(a & 0xFFFFu), (unsigned short)(a >> 16)};
-                m = __builtin_elementwise_max(m, v);
-            }
+            for (int i = 0; i < WORDS; ++i)
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
             unsigned short h = m.x > m.y ? m.x : m.y;
             if constexpr (DT == ZPQ_F16)
                 return __float_as_uint(__half2float(__ushort_as_half(h)));
@@ -435,15 +374,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_i8(const void* __restrict__ 
         const int64_t e = wg_base + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
         if (e < n) tile[u].template load<ZPQ_NTL_QUANT>(x, e); else tile[u].zero();
     }
-    // Every tile's block scale first, so that the scale-table loads of all
-    // tiles are in flight together, then the codes.
+    // Every tile's block scale first (the divisions of the tiles are
+    // independent and interleave), then the codes.
     BlockScale<127, DT != ZPQ_F32> bss[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) bss[u] = tile[u].template block_scale<127, G>();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t e = wg_base + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
-        const auto& bs = bss[u];
+        auto& bs = bss[u];
         float v[EPL];
 #pragma unroll
         for (int k = 0; k < EPL; ++k) v[k] = tile[u].get(k);
@@ -525,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_tensor_codes(const void* __restric
     constexpr int EPL = kTensorEpl;
     const float s = scale[0];
     const bool fast = s >= 0x1p-100f;
-    const BlockScale<127, DT != ZPQ_F32> bs(s, fast ? 1.0f / s : 0.0f);
+    const float r = fast ? 1.0f / s : 0.0f;
     const int64_t base = (int64_t)blockIdx.x * kTensorTile;
     InTile<DT, EPL> tile[kTensorU];
 #pragma unroll
@@ -540,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void k_tensor_codes(const void* __restric
 #pragma unroll
         for (int k = 0; k < EPL; ++k) v[k] = tile[u].get(k);
         uint32_t q[EPL];
-        bs.codes(v, q);
+        codes_of<127, DT != ZPQ_F32>(s, r, fast, v, q);
         if (e < n)
             st_stream<false>(u32x2{pack_low_bytes(q[0], q[1], q[2], q[3]),
                                    pack_low_bytes(q[4], q[5], q[6], q[7])},
@@ -656,15 +595,15 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
         const int64_t f = f0 + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
         if (f < S) tile[u].template load<ZPQ_NTL_QGZ>(grad, src0 + f); else tile[u].zero();
     }
-    // Every tile's block scale first, so that the scale-table loads of all
-    // tiles are in flight together, then the codes.
+    // Every tile's block scale first (the divisions of the tiles are
+    // independent and interleave), then the codes.
     BlockScale<7, DT != ZPQ_F32> bss[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) bss[u] = tile[u].template block_scale<7, G>();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t f = f0 + (int64_t)u * (kThreads * EPL) + threadIdx.x * EPL;
-        const auto& bs = bss[u];
+        auto& bs = bss[u];
         float v[EPL];
 #pragma unroll
         for (int k = 0; k < EPL; ++k) v[k] = tile[u].get(k);

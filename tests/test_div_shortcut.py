@@ -1,9 +1,12 @@
-"""The GPU quantizer's division shortcut for 16-bit inputs, checked by
+"""The GPU quantizer's arithmetic shortcuts for 16-bit inputs, checked by
 exhaustion on the CPU (tests/div_check.c): for every positive finite fp16 or
-bf16 absmax a with s = fl32(a/qmax) >= 2^-100 and every value 0 <= x <= a of
-the same type, one residual correction of x * fl32(1/s) rounds to the same
-integer as the IEEE quotient fl32(x/s).  (fp32 inputs use two corrections,
-which Markstein's theorem makes exact without enumeration.)"""
+bf16 absmax a, the scale fl32(a/qmax) from a product and one residual
+correction (a >= 2^-90) equals the IEEE quotient; and for every a with
+s = fl32(a/qmax) >= 2^-100, every value 0 <= x <= a of the same type and
+either float next to the exact 1/s, one residual correction of x * r rounds
+to the same integer as the IEEE quotient fl32(x/s).  (fp32 inputs use two
+corrections with the correctly rounded reciprocal, which Markstein's theorem
+makes exact without enumeration.)"""
 import os
 import subprocess
 
@@ -28,4 +31,6 @@ def test_one_correction_is_exact_for_16bit_inputs(checker, dtype, qmax):
     out = subprocess.run([checker, dtype, str(qmax), threads], check=True, capture_output=True,
                          text=True).stdout.split()
     assert out[0] == "mismatches" and int(out[1]) == 0, out
-    assert int(out[3]) > 5 * 10 ** 8          # about half of all (a, x) pairs, x >= 0
+    assert int(out[3]) > 10 ** 9              # about half of all (a, x) pairs, x >= 0, two r each
+    assert out[4] == "scale_mismatches" and int(out[5]) == 0, out
+    assert int(out[7]) > 27000                 # every absmax >= 2^-90
