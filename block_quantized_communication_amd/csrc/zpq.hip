@@ -88,13 +88,13 @@
 #define ZPQ_NTL_QUANT 1
 #endif
 #ifndef ZPQ_NTS_QUANT
-#define ZPQ_NTS_QUANT 0
+#define ZPQ_NTS_QUANT 1
 #endif
 #ifndef ZPQ_NTL_DEQUANT
 #define ZPQ_NTL_DEQUANT 1
 #endif
 #ifndef ZPQ_NTS_DEQUANT
-#define ZPQ_NTS_DEQUANT 0
+#define ZPQ_NTS_DEQUANT 1
 #endif
 #ifndef ZPQ_NTL_QGZ
 #define ZPQ_NTL_QGZ 1
