@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.5)
+    ap.add_argument("--per-config", action="store_true",
+                    help="time every kernel at every workload size (cache evicted before each "
+                         "launch) instead of the step")
     ap.add_argument("--study", choices=["hop-count", "blocking"], default=None,
                     help="run an error study instead of the throughput benchmark")
     ap.add_argument("--copy-probe", action="store_true",
@@ -74,6 +77,9 @@ def main():
         return
     if args.study == "blocking":
         print(json.dumps(blocking_study(np, torch, zpq, synth)), flush=True)
+        return
+    if args.per_config:
+        print(json.dumps(per_config(np, torch, zpq, synth)), flush=True)
         return
 
     torch.cuda.set_device(0)
@@ -347,6 +353,121 @@ def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):
     return {"study": "hop-count error: qgZ two-hop all-to-all vs compressed ring "
                      "reduce-scatter (INT4, block 128)", "slice_elems": S, "rows": rows,
             "error": "RMS(y - exact mean) / RMS(exact mean), fp64 reference"}
+
+
+def per_config(np, torch, zpq, synth, reps=30, settle_s=0.2):
+    """Every kernel at every workload size, one launch at a time: before each
+    timed launch a read-only pass over 1 GiB of scratch evicts the 256 MB
+    last-level cache (reads leave no dirty lines behind to be written back
+    during the timed kernel); each launch is bracketed by HIP events on its
+    stream; median and minimum over `reps` launches after a settle phase.
+    Inputs are the workloads' generators; the receive buffers of the hop
+    kernels are filled by the send-side kernels (timing needs realistic codes,
+    not oracle values: parity at these sizes is the GPU tests' job)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T = torch
+    st = torch.cuda.current_stream()
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    rows = []
+
+    def timed(label, fn, nbytes):
+        def evict():
+            scratch.max()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(5):
+                evict()
+                fn()
+            torch.cuda.synchronize()
+        us = []
+        for _ in range(reps):
+            evict()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3)
+        med = float(np.median(us))
+        rows.append({"kernel": label, "bytes": int(nbytes), "us_median": round(med, 2),
+                     "us_min": round(float(min(us)), 2),
+                     "GBps": round(nbytes / med / 1e3, 1),
+                     "frac_of_peak": round(nbytes / med / 1e3 / HBM_PEAK_GBS, 4)})
+        print(f"[per-config] {label}: {med:.1f} us, {nbytes / med / 1e3:.0f} GB/s",
+              file=sys.stderr, flush=True)
+
+    e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
+    # c1: qwZ round trip, 2^20 fp16, B = 256 (launch-bound)
+    c = synth.QWZ_ROUNDTRIP
+    n, B = c["n"], c["block"]
+    x = torch.from_numpy(synth.qwz_roundtrip()).to(dev)
+    cc, cs, y = e(n, T.int8), e(n // B, T.float32), e(n, T.float16)
+    nb = n * 2 + n + n // B * 4
+    timed("c1 K1 quant_i8 2^20 fp16 B=256", lambda: zpq.quant_i8(x, B, out=(cc, cs), stream=st), nb)
+    timed("c1 K2 dequant_i8 2^20 -> fp16", lambda: zpq.dequant_i8(cc, cs, B, out=y, stream=st), nb)
+    del x, cc, cs, y
+    # c2: qwZ on the h8192 layer, 16 ranks
+    c = synth.QWZ_LAYER
+    n, B, W = c["n"], c["block"], c["world"]
+    S = n // W
+    layer = torch.from_numpy(synth.qwz_layer()).to(dev)
+    sc, ss = e(S, T.int8), e(S // B, T.float32)
+    gc, gs, y = e(n, T.int8), e(n // B, T.float32), e(n, T.float16)
+    zpq.quant_i8(layer, B, out=(gc, gs), stream=st)
+    timed("c2 K1 quant_i8 shard 50.3M fp16 B=256",
+          lambda: zpq.quant_i8(layer[:S], B, out=(sc, ss), stream=st), S * 3 + S // B * 4)
+    timed("c2 K2 dequant_i8 gathered 805M -> fp16",
+          lambda: zpq.dequant_i8(gc, gs, B, out=y, stream=st), n * 3 + n // B * 4)
+    del layer, sc, ss, gc, gs, y
+    # c3: qgZ hop 1, bf16 2^28, L = 8, N = 4, B = 128
+    c = synth.QGZ_HOP1
+    n, B, L, N = c["n"], c["block"], c["L"], c["N"]
+    chunk = n // L
+    g = torch.from_numpy(synth.qgz_hop1()).view(T.bfloat16).to(dev)
+    c1, s1 = e(n // 2, T.uint8), e(n // B, T.float32)
+    c2, s2 = e(chunk // 2, T.uint8), e(chunk // B, T.float32)
+    timed("c3 K3 reorder_quant_i4 2^28 bf16 L=8 N=4 B=128",
+          lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1), stream=st),
+          n * 2 + n // 2 + n // B * 4)
+    timed("c3 K4 hop-1 8 x 2^25 -> INT4",
+          lambda: zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B, out=(c2, s2), stream=st),
+          L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4)
+    del g, c1, s1, c2, s2
+    # c4: qgZ hop 2, 16 sources x 2^24, bf16 average
+    c = synth.QGZ_HOP2
+    K, chunk, B = c["sources"], c["chunk"], c["block"]
+    src = torch.from_numpy(np.concatenate([synth.qgz_hop2_source(i) for i in range(K)])).to(dev)
+    ic, isc = zpq.qgz_reorder_quant_i4(src, 1, 1, B)
+    del src
+    y = e(chunk, T.bfloat16)
+    timed("c4 K5 hop-2 16 x 2^24 -> bf16 average",
+          lambda: zpq.qgz_dequant_reduce_requant_i4(ic, isc, K, chunk, B, out_dtype=T.bfloat16,
+                                                    divisor=c["divisor"], out=y, stream=st),
+          K * (chunk // 2 + chunk // B * 4) + chunk * 2)
+    del ic, isc, y
+    # c5: fused qgZ on the 138B-model layer gradient, L = 8, N = 48, B = 64
+    c = synth.QGZ_FUSED
+    n, B, L, N = c["n"], c["block"], c["L"], c["N"]
+    W = L * N
+    S, chunk = n // W, n // L
+    g = torch.from_numpy(synth.qgz_fused()).to(dev)
+    c1, s1 = e(n // 2, T.uint8), e(n // B, T.float32)
+    c2, s2 = e(chunk // 2, T.uint8), e(chunk // B, T.float32)
+    y = e(S, T.float16)
+    timed("c5 K3 reorder_quant_i4 1.06G fp16 L=8 N=48 B=64",
+          lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1), stream=st),
+          n * 2 + n // 2 + n // B * 4)
+    timed("c5 K4 hop-1 8 x 132M -> INT4",
+          lambda: zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B, out=(c2, s2), stream=st),
+          L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4)
+    timed("c5 K5 hop-2 48 x 2.75M -> fp16 average",
+          lambda: zpq.qgz_dequant_reduce_requant_i4(c2, s2, N, S, B, out_dtype=T.float16,
+                                                    divisor=float(W), out=y, stream=st),
+          N * (S // 2 + S // B * 4) + S * 2)
+    return {"per_config": rows, "timing": f"median of {reps} single launches, HIP events, "
+            "1 GiB read-only pass before each launch, 200 ms settle per kernel",
+            "peak_GBps": HBM_PEAK_GBS}
 
 
 def blocking_study(np, torch, zpq, synth, reps=20):

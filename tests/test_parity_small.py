@@ -84,7 +84,7 @@ def test_qgz_reorder_quant_i4(dtype, block, L, N):
 def random_received(rng, K, chunk, block, huge=False):
     """K received INT4 chunks: random nibbles and scales of every class.
     Without `huge`, nibbles cover all 16 values (-8 included: any nibble
-    decodes).  With `huge`, some scales exceed FLT_MAX/8 (so 8*s overflows)
+    decodes) and some scales exceed 2^100 (up to 1e32).  With `huge`, some scales exceed FLT_MAX/8 (so 8*s overflows)
     and nibbles stay in [-7, 7], as the quantizer produces, so that every true
     sum stays finite."""
     if huge:
@@ -97,6 +97,9 @@ def random_received(rng, K, chunk, block, huge=False):
         np.float32)
     s[:, ::9] = 0.0
     s[:, 1::9] = np.float32(1e-40)
+    if not huge:
+        s[:, 3::9] = np.float32(1e32)            # s * 2^24 overflows fp32; sums stay finite
+        s[:, 4::9] = np.float32(3e30)            # just above 2^100
     if huge:
         s[0, 2::9] = np.float32(4.5e37)         # 8 * s overflows; 7 * s does not
         s[1:, 2::9] = 0.0                        # keep the true sums finite
