@@ -44,7 +44,7 @@ def parse():
                          "state")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--cpu-fraction", type=float, default=0.5)
+    ap.add_argument("--cpu-fraction", type=float, default=0.6)
     ap.add_argument("--per-config", action="store_true",
                     help="time every kernel at every workload size (cache evicted before each "
                          "launch) instead of the step")

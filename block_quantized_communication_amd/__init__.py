@@ -56,8 +56,8 @@ def lib():
         L.zpq_qgz_reorder_quant_i4.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp]
         L.zpq_qgz_dequant_reduce_requant_i4.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32,
                                                         f32, vp]
-        for f in (L.zpq_quant_i8, L.zpq_dequant_i8, L.zpq_qgz_reorder_quant_i4,
-                  L.zpq_qgz_dequant_reduce_requant_i4):
+        for f in (L.zpq_quant_i8, L.zpq_dequant_i8, L.zpq_quant_i8_tensor,
+                  L.zpq_qgz_reorder_quant_i4, L.zpq_qgz_dequant_reduce_requant_i4):
             f.restype = ctypes.c_int
         L.zpq_status_str.argtypes = [ctypes.c_int]
         L.zpq_status_str.restype = ctypes.c_char_p

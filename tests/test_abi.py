@@ -147,3 +147,22 @@ def test_binding_refuses_bad_tensors():
     with pytest.raises(ValueError):
         zpq.quant_i8(x, 256, out=(torch.zeros(1024, dtype=torch.int8),
                                   torch.zeros(4, dtype=torch.float32)))
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without the built HIP library every entry point raises."""
+    monkeypatch.setattr(zpq, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libzpq.so"))
+    monkeypatch.setattr(zpq, "_lib", None)
+    with pytest.raises(ImportError):
+        zpq.lib()
+    with pytest.raises(ImportError):
+        zpq.abi_version()
+
+
+def test_bench_measures_one_gpu_only():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
