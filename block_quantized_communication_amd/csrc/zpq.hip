@@ -63,7 +63,13 @@
 #define ZPQ_REDUCE_PF_I4 4     // received sources in flight per lane (hop 1)
 #endif
 #ifndef ZPQ_REDUCE_PF_FL
-#define ZPQ_REDUCE_PF_FL 8     // received sources in flight per lane (hop 2)
+#define ZPQ_REDUCE_PF_FL 2     // received sources in flight per lane (hop 2)
+#endif
+#ifndef ZPQ_REDUCE_PF_FL_NARROW
+#define ZPQ_REDUCE_PF_FL_NARROW 4  // the same with 8 elements per lane (short chunks)
+#endif
+#ifndef ZPQ_REDUCE_NARROW_WAVES
+#define ZPQ_REDUCE_NARROW_WAVES 8  // hop 2: 8 elements per lane below this many waves per SIMD
 #endif
 // Persistent grids: workgroups per compute unit (0 = one workgroup per
 // virtual block, no loop).
@@ -908,6 +914,7 @@ constexpr int kEplDequant = ZPQ_DEQUANT_EPL, kUDequant = ZPQ_DEQUANT_U;
 constexpr int kEplQgz = ZPQ_QGZ_EPL, kUQgz = ZPQ_QGZ_U;
 constexpr int kEplI4 = ZPQ_REDUCE_EPL_I4, kEplFl = ZPQ_REDUCE_EPL_FL;
 constexpr int kPfI4 = ZPQ_REDUCE_PF_I4, kPfFl = ZPQ_REDUCE_PF_FL;
+constexpr int kPfFlNarrow = ZPQ_REDUCE_PF_FL_NARROW;
 
 template <int DT, int BLOCK>
 void launch_quant_dt(const void* x, int64_t n, int8_t* codes, float* scales, hipStream_t st) {
@@ -980,6 +987,22 @@ zpq_status launch_qgz_quant(const void* g, int32_t dt, int64_t n, int32_t L, int
 template <int BLOCK, int EPL>
 constexpr int epl_for() { return EPL <= BLOCK ? EPL : BLOCK; }
 
+template <int BLOCK, int EPL, int PF>
+void launch_reduce_fl(const uint8_t* ic, const float* is, int32_t K, int64_t c, void* ov,
+                      int32_t odt, float divisor, float rdiv, bool div_fast, hipStream_t st) {
+    const unsigned nvb = grid_for(c, (int64_t)kThreads * EPL);
+    const dim3 grid(launch_grid(nvb, ZPQ_PERSIST_REDUCE));
+    if (odt == ZPQ_F32)
+        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EPL, ZPQ_F32, PF>), grid, dim3(kThreads), 0,
+                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, div_fast, nvb);
+    else if (odt == ZPQ_F16)
+        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EPL, ZPQ_F16, PF>), grid, dim3(kThreads), 0,
+                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, div_fast, nvb);
+    else
+        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EPL, ZPQ_BF16, PF>), grid, dim3(kThreads), 0,
+                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, div_fast, nvb);
+}
+
 template <int BLOCK>
 zpq_status launch_reduce(const uint8_t* ic, const float* is, int32_t K, int64_t c, uint8_t* oc,
                          float* os, void* ov, int32_t odt, float divisor, hipStream_t st) {
@@ -993,21 +1016,14 @@ zpq_status launch_reduce(const uint8_t* ic, const float* is, int32_t K, int64_t 
                            is, K, c, oc, os, ov, divisor, rdiv, div_fast, nvb);
         return after_launch();
     }
-    const unsigned nvb = grid_for(c, (int64_t)kThreads * EF);
-    const dim3 grid(launch_grid(nvb, ZPQ_PERSIST_REDUCE));
-    if (odt == ZPQ_F32) {
-        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EF, ZPQ_F32, kPfFl>), grid,
-                           dim3(kThreads), 0, st, ic, is, K, c, oc, os, ov, divisor, rdiv,
-                           div_fast, nvb);
-    } else if (odt == ZPQ_F16) {
-        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EF, ZPQ_F16, kPfFl>), grid,
-                           dim3(kThreads), 0, st, ic, is, K, c, oc, os, ov, divisor, rdiv,
-                           div_fast, nvb);
-    } else {
-        hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EF, ZPQ_BF16, kPfFl>), grid,
-                           dim3(kThreads), 0, st, ic, is, K, c, oc, os, ov, divisor, rdiv,
-                           div_fast, nvb);
-    }
+    // A short chunk gives few waves at 16 elements per lane (the fused
+    // workload's hop 2: 2.6 per SIMD); halving the lane's share doubles them.
+    const int64_t waves16 = (c + 16 * 64 - 1) / (16 * 64);
+    if (BLOCK <= 256 && waves16 < (int64_t)ZPQ_REDUCE_NARROW_WAVES * 4 * cu_count())
+        launch_reduce_fl<BLOCK, 8, kPfFlNarrow>(ic, is, K, c, ov, odt, divisor, rdiv, div_fast,
+                                                st);
+    else
+        launch_reduce_fl<BLOCK, EF, kPfFl>(ic, is, K, c, ov, odt, divisor, rdiv, div_fast, st);
     return after_launch();
 }
 

@@ -125,7 +125,7 @@ def test_dequant_reduce_requant_i4(block, K):
 
 
 @pytest.mark.parametrize("out", DTYPES)
-@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("block", [32, 64, 128, 512])
 @pytest.mark.parametrize("K,divisor", [(1, 1.0), (3, 3.0), (16, 16.0), (48, 384.0),
                                        (8, 0.5), (5, 2.0 ** 50), (4, 1e-30)])
 def test_dequant_reduce_average(out, block, K, divisor):
@@ -141,6 +141,20 @@ def test_dequant_reduce_average(out, block, K, divisor):
                                                out_dtype=torch_dt(out), divisor=divisor)
         ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, out, divisor)
         assert_bits_equal(from_device(y), ref, "values")
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_dequant_reduce_average_long_chunk(out):
+    """A chunk long enough for the hop-2 launch with 16 elements per lane
+    (short chunks take 8 per lane): 2^23 + 2^16 elements, 3 sources."""
+    rng = np.random.default_rng(77)
+    K, block, chunk = 3, 128, (1 << 23) + (1 << 16)
+    codes, s = random_received(rng, K, chunk, block)
+    print(f"dequant_reduce_average long chunk out={out} K={K} chunk={chunk}", flush=True)
+    y = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk, block,
+                                           out_dtype=torch_dt(out), divisor=3.0)
+    ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, out, 3.0)
+    assert_bits_equal(from_device(y), ref, "values")
 
 
 def test_requant_single_source_is_identity():
