@@ -11,9 +11,12 @@
 //                                   them in fp32 in source order, then INT4
 //                                   requantize (hop 1) or average (hop 2)
 // (ZeRO++ summary page, atlas.scime.ai, "Approach"; mlsanity.com index page,
-// "Abstract (arXiv)"; LIT-102 anthology record, "Key takeaways".)
+// "Abstract (arXiv)"; LIT-102 anthology record, "Key takeaways".)  Plus the
+// non-blocked ablation (zpq_quant_i8_tensor: one scale per tensor, the
+// summary page's "Measured effects" table and "Surprising findings").
 //
-// Every kernel streams HBM once: 128-bit loads, one quantization block per
+// Every kernel streams HBM once (the per-tensor quantizer twice: it needs the
+// tensor's maximum before the first code): wide vector loads, one quantization block per
 // aligned group of BLOCK/EPL lanes of a wave64 (EPL = elements per lane),
 // the block absmax reduced with DPP lane permutes, the division done as a
 // correctly rounded multiply-and-correct sequence, codes packed in registers
@@ -30,6 +33,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "zpq.h"
 
@@ -185,10 +190,11 @@ __device__ __forceinline__ uint32_t round_code(float t) {
     return __float_as_uint(t + 12582912.0f);
 }
 
-// fl32(x / s) after ONE residual correction.  For fp16 and bf16 inputs
-// (x and the block absmax both 16-bit values) this rounds to the same integer
-// code as the IEEE quotient: checked by exhaustion over every absmax and
-// every |x| <= absmax of both types, for qmax 127 and 7.
+// fl32(x / s) after ONE residual correction, r within one ulp of 1/s.  For
+// fp16 and bf16 inputs (x and the block absmax both 16-bit values, s their
+// scale) this rounds to the same integer code as the IEEE quotient: checked by
+// exhaustion over every absmax, every |x| <= absmax of both types and both
+// floats next to 1/s, for qmax 127 and 7.
 __device__ __forceinline__ float div_1c(float x, float s, float r) {
     const float q = x * r;
     return __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
@@ -880,20 +886,25 @@ inline unsigned grid_for(int64_t elems, int64_t per_wg) {
     return (unsigned)((elems + per_wg - 1) / per_wg);
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; host threads
+// may race to fill an entry, with the same value).
 inline int cu_count() {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
+
+// Element counts above 2^40 are refused (ZPQ_ERR_SIZE): grid sizes stay
+// within 32 bits and byte counts within 64.
+constexpr int64_t kMaxElems = 1LL << 40;
 
 // Launch grid for nvb virtual blocks: all of them, or a persistent grid of
 // per_cu workgroups per compute unit that loops over them.
@@ -985,7 +996,9 @@ zpq_status launch_qgz_quant(const void* g, int32_t dt, int64_t n, int32_t L, int
 }
 
 template <int BLOCK, int EPL>
-constexpr int epl_for() { return EPL <= BLOCK ? EPL : BLOCK; }
+constexpr int epl_for() {
+    return EPL > BLOCK ? BLOCK : (BLOCK / EPL <= 32 ? EPL : BLOCK / 32);   // a block spans <= 32 lanes
+}
 
 template <int BLOCK, int EPL, int PF>
 void launch_reduce_fl(const uint8_t* ic, const float* is, int32_t K, int64_t c, void* ov,
@@ -1043,7 +1056,7 @@ extern "C" {
 zpq_status zpq_quant_i8(const void* x, int32_t x_dtype, int64_t n, int32_t block, int8_t* codes,
                         float* scales, zpq_stream stream) {
     if (!block_ok(block)) return ZPQ_ERR_BLOCK;
-    if (n < 0 || n % block != 0) return ZPQ_ERR_SIZE;
+    if (n < 0 || n > kMaxElems || n % block != 0) return ZPQ_ERR_SIZE;
     const int64_t eb = dtype_bytes(x_dtype);
     if (eb == 0) return ZPQ_ERR_DTYPE;
     if (n == 0) return ZPQ_OK;
@@ -1059,7 +1072,7 @@ zpq_status zpq_quant_i8(const void* x, int32_t x_dtype, int64_t n, int32_t block
 
 zpq_status zpq_quant_i8_tensor(const void* x, int32_t x_dtype, int64_t n, int8_t* codes,
                                float* scale, zpq_stream stream) {
-    if (n < 0 || n % 16 != 0) return ZPQ_ERR_SIZE;
+    if (n < 0 || n > kMaxElems || n % 16 != 0) return ZPQ_ERR_SIZE;
     const int64_t eb = dtype_bytes(x_dtype);
     if (eb == 0) return ZPQ_ERR_DTYPE;
     if (!scale) return ZPQ_ERR_NULL;
@@ -1111,7 +1124,7 @@ zpq_status zpq_quant_i8_tensor(const void* x, int32_t x_dtype, int64_t n, int8_t
 zpq_status zpq_dequant_i8(const int8_t* codes, const float* scales, int64_t n, int32_t block,
                           void* y, int32_t y_dtype, zpq_stream stream) {
     if (!block_ok(block)) return ZPQ_ERR_BLOCK;
-    if (n < 0 || n % block != 0) return ZPQ_ERR_SIZE;
+    if (n < 0 || n > kMaxElems || n % block != 0) return ZPQ_ERR_SIZE;
     const int64_t eb = dtype_bytes(y_dtype);
     if (eb == 0) return ZPQ_ERR_DTYPE;
     if (n == 0) return ZPQ_OK;
@@ -1130,7 +1143,7 @@ zpq_status zpq_qgz_reorder_quant_i4(const void* grad, int32_t g_dtype, int64_t n
     if (local_ranks < 1 || nodes < 1) return ZPQ_ERR_ARG;
     const int64_t W = (int64_t)local_ranks * nodes;
     if (W > 0x7FFFFFFF) return ZPQ_ERR_ARG;
-    if (n < 0 || n % (W * block) != 0) return ZPQ_ERR_SIZE;
+    if (n < 0 || n > kMaxElems || n % (W * block) != 0) return ZPQ_ERR_SIZE;
     const int64_t eb = dtype_bytes(g_dtype);
     if (eb == 0) return ZPQ_ERR_DTYPE;
     if (n == 0) return ZPQ_OK;

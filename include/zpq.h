@@ -29,7 +29,8 @@
  *     and input and output ranges disjoint; sizes non-negative and whole
  *     blocks (callers pad, as ZeRO pads partitions); block in
  *     {32, 64, 128, 256, 512}; element types valid.
- *   - Element counts are 64-bit; buffers above 2^31 bytes are supported.
+ *   - Element counts are 64-bit, at most 2^40 (else ZPQ_ERR_SIZE); buffers
+ *     above 2^31 bytes are supported.
  *   - ZPQ_ERR_LAUNCH reports a launch failure from the HIP runtime (for
  *     example a device other than gfx950).
  *   - Calls that write the same output concurrently race; calls on one

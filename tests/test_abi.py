@@ -61,6 +61,7 @@ def test_quant_i8_validation():
     assert q8(codes=P + 1024) == ALIAS          # codes inside x's 2 KB
     assert q8(scales=P + (1 << 16) + 512) == ALIAS
     assert q8(n=0, x=0, codes=0, scales=0) == OK   # empty: nothing to do
+    assert q8(n=(1 << 40) + 256) == SIZE             # beyond the element limit
 
 
 def dq8(codes=P, scales=P + (1 << 16), n=1024, block=256, y=P + (1 << 18), dt=1):
@@ -75,6 +76,7 @@ def test_dequant_i8_validation():
     assert dq8(scales=P + (1 << 16) + 4) == ALIGN
     assert dq8(y=P + 512) == ALIAS
     assert dq8(n=0, codes=0, scales=0, y=0) == OK
+    assert dq8(n=(1 << 40) + 256) == SIZE
 
 
 def qt8(x=P, dt=2, n=1024, codes=P + (1 << 16), scale=P + (1 << 18)):
@@ -84,6 +86,7 @@ def qt8(x=P, dt=2, n=1024, codes=P + (1 << 16), scale=P + (1 << 18)):
 def test_quant_i8_tensor_validation():
     assert qt8(n=1000) == SIZE
     assert qt8(n=-16) == SIZE
+    assert qt8(n=(1 << 40) + 16) == SIZE
     assert qt8(dt=5) == DTYPE
     assert qt8(scale=0) == NULL
     assert qt8(x=0) == NULL
@@ -110,6 +113,7 @@ def test_qgz_reorder_quant_validation():
     assert rq4(codes=P + (1 << 18) + 8) == ALIGN
     assert rq4(codes=P + 4096) == ALIAS
     assert rq4(n=0, g=0, codes=0, scales=0) == OK
+    assert rq4(n=(1 << 40) + 8 * 4 * 128) == SIZE
 
 
 def dr4(ic=P, isc=P + (1 << 18), K=8, c=4096, block=128, oc=P + (1 << 19),
