@@ -422,12 +422,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_i8(const void* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Per-tensor INT8 quantization (non-blocked ablation): three passes.
-//  1. every workgroup writes the bit pattern of its max |x| into slot vb of a
-//     uint32 array that overlays the codes buffer (overwritten in pass 3);
-//  2. one workgroup reduces those maxima and writes s = fl32(a/127);
+//  1. at most kTensorPartials workgroups loop over the tiles; each writes the
+//     bit pattern of its max |x| into its slot of a uint32 array that
+//     overlays the codes buffer (overwritten in pass 3);
+//  2. one workgroup reduces those maxima (all loads issued at once) and
+//     writes s = fl32(a/127);
 //  3. the codes, with that one scale (the block quantizer's code path).
 constexpr int kTensorEpl = 8, kTensorU = 2;
 constexpr int64_t kTensorTile = (int64_t)kTensorU * kThreads * kTensorEpl;
+constexpr int kTensorPartials = 2048;
+static_assert(kTensorPartials % kThreads == 0, "whole loads per thread");
 
 // max over a workgroup of per-lane values (bit patterns of non-negative floats)
 __device__ __forceinline__ uint32_t workgroup_max(uint32_t v) {
@@ -445,16 +449,19 @@ __device__ __forceinline__ uint32_t workgroup_max(uint32_t v) {
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_tensor_absmax(const void* __restrict__ x, int64_t n,
+                                                            int64_t ntiles,
                                                             uint32_t* __restrict__ partial) {
-    const int64_t base = (int64_t)blockIdx.x * kTensorTile;
     uint32_t m = 0;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t base = tile * kTensorTile;
 #pragma unroll
-    for (int u = 0; u < kTensorU; ++u) {
-        const int64_t e = base + (int64_t)u * (kThreads * kTensorEpl) + threadIdx.x * kTensorEpl;
-        if (e < n) {
-            InTile<DT, kTensorEpl> t;
-            t.template load<true>(x, e);
-            m = max(m, t.absmax_bits());
+        for (int u = 0; u < kTensorU; ++u) {
+            const int64_t e = base + (int64_t)u * (kThreads * kTensorEpl) + threadIdx.x * kTensorEpl;
+            if (e < n) {
+                InTile<DT, kTensorEpl> t;
+                t.template load<true>(x, e);
+                m = max(m, t.absmax_bits());
+            }
         }
     }
     m = workgroup_max(m);
@@ -462,9 +469,13 @@ __global__ __launch_bounds__(kThreads) void k_tensor_absmax(const void* __restri
 }
 
 __global__ __launch_bounds__(kThreads) void k_tensor_scale(const uint32_t* __restrict__ partial,
-                                                           int64_t count, float* __restrict__ scale) {
+                                                           int32_t count, float* __restrict__ scale) {
     uint32_t m = 0;
-    for (int64_t i = threadIdx.x; i < count; i += kThreads) m = max(m, partial[i]);
+#pragma unroll
+    for (int k = 0; k < kTensorPartials / kThreads; ++k) {
+        const int i = k * kThreads + threadIdx.x;
+        if (i < count) m = max(m, partial[i]);
+    }
     m = workgroup_max(m);
     if (threadIdx.x == 0) scale[0] = __uint_as_float(m) / 127.0f;
 }
@@ -1082,26 +1093,26 @@ zpq_status zpq_quant_i8_tensor(const void* x, int32_t x_dtype, int64_t n, int8_t
         overlaps(codes, n, scale, 4))
         return ZPQ_ERR_ALIAS;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t nwg = (n + kTensorTile - 1) / kTensorTile;
-    if (nwg > 0x7FFFFFFFLL) return ZPQ_ERR_SIZE;
-    uint32_t* partial = reinterpret_cast<uint32_t*>(codes);     // nwg * 4 <= n bytes
-    if (nwg > 0) {
+    const int64_t nwg = (n + kTensorTile - 1) / kTensorTile;           // tiles of the codes pass
+    const int32_t np = (int32_t)(nwg < kTensorPartials ? nwg : kTensorPartials);
+    uint32_t* partial = reinterpret_cast<uint32_t*>(codes);     // np * 4 <= n bytes
+    if (np > 0) {
         switch (x_dtype) {
         case ZPQ_F32:
-            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_F32>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
-                               x, n, partial);
+            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_F32>, dim3(np), dim3(kThreads), 0, st, x, n,
+                               nwg, partial);
             break;
         case ZPQ_F16:
-            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_F16>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
-                               x, n, partial);
+            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_F16>, dim3(np), dim3(kThreads), 0, st, x, n,
+                               nwg, partial);
             break;
         default:
-            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_BF16>, dim3((unsigned)nwg), dim3(kThreads), 0,
-                               st, x, n, partial);
+            hipLaunchKernelGGL(k_tensor_absmax<ZPQ_BF16>, dim3(np), dim3(kThreads), 0, st, x, n,
+                               nwg, partial);
             break;
         }
     }
-    hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(kThreads), 0, st, partial, nwg, scale);
+    hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(kThreads), 0, st, partial, np, scale);
     if (nwg > 0) {
         switch (x_dtype) {
         case ZPQ_F32:

@@ -279,9 +279,10 @@ def test_ring_reduce_scatter_chain_matches_oracle():
 @pytest.mark.parametrize("kind", ["outliers", "adversarial", "tiny", "zero", "max_last"])
 def test_quant_i8_tensor(dtype, kind):
     """Per-tensor INT8 quantization equals the oracle's block quantizer with
-    one block spanning the tensor, for one to several hundred workgroups."""
+    one block spanning the tensor, from one tile to more tiles than the
+    absmax pass has workgroups."""
     rng = np.random.default_rng(len(kind) * 3 + len(dtype))
-    for n in (16, 3 * 4096 + 16, (1 << 18) + 48, 3 << 20):
+    for n in (16, 3 * 4096 + 16, (1 << 18) + 48, 3 << 20, (9 << 20) + 16):   # last: > 2048 tiles
         if kind == "outliers":
             x = (rng.standard_normal(n) * 0.02).astype(np.float32)
             pos = rng.integers(0, n, max(1, n // 1000))
