@@ -104,6 +104,11 @@ def main():
     grad_h = synth.qgz_fused()
     grad = torch.from_numpy(grad_h).to(dev)
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    import hashlib
+    inputs = {"qwz_layer": {"seed": synth.SEEDS["qwz_layer"],
+                            "sha256": hashlib.sha256(memoryview(layer_h).cast("B")).hexdigest()},
+              "qgz_grad": {"seed": synth.SEEDS["qgz_fused"],
+                           "sha256": hashlib.sha256(memoryview(grad_h).cast("B")).hexdigest()}}
 
     shard = layer[:Sw]
     e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
@@ -240,6 +245,7 @@ def main():
                         "hidden 8192 (fp16, INT8 block 256, 16 ranks) + qgZ on a 138B-model "
                         "layer gradient (fp16, INT4 block 64, L=8, N=48, both hops)",
             "qwz_layer_elems": nw, "qwz_shard_elems": Sw, "qgz_grad_elems": ng,
+            "inputs": inputs,
             "step_bytes": step_bytes, "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
             "kernels": rows,
             "parity": check,
