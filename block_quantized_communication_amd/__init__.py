@@ -81,7 +81,10 @@ def _torch():
 
 def dtype_code(dt):
     torch = _torch()
-    return {torch.float32: ZPQ_F32, torch.float16: ZPQ_F16, torch.bfloat16: ZPQ_BF16}[dt]
+    codes = {torch.float32: ZPQ_F32, torch.float16: ZPQ_F16, torch.bfloat16: ZPQ_BF16}
+    if dt not in codes:
+        raise ValueError(f"unsupported element type {dt} (float32, float16 or bfloat16)")
+    return codes[dt]
 
 
 def torch_dtype(code):
@@ -93,9 +96,9 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _stream(stream):
+def _stream(stream, device):
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -104,26 +107,40 @@ def _check(rc, where):
         raise ZpqError(rc, where)
 
 
-def _need(t, dtype, numel, name):
-    if t.dtype != dtype or t.numel() != numel or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name}: need a contiguous CUDA {dtype} tensor of {numel} elements, "
-                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+def _gpu(t, name, device=None):
+    """t must be a contiguous tensor on a GPU (on `device` when given): the
+    library receives raw device pointers and checks neither."""
+    if not t.is_cuda or not t.is_contiguous() or (device is not None and t.device != device):
+        where = "a GPU" if device is None else str(device)
+        raise ValueError(f"{name}: need a contiguous tensor on {where}, got "
+                         f"{tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+    return t.device
+
+
+def _need(t, dtype, numel, name, device):
+    _gpu(t, name, device)
+    if t.dtype != dtype or t.numel() != numel:
+        raise ValueError(f"{name}: need {numel} elements of {dtype}, got {t.numel()} of {t.dtype}")
+
+
+def _blocks(n, block):
+    return n // block if block > 0 else 0       # a bad block is refused by the library
 
 
 def quant_i8(x, block=256, out=None, stream=None):
     """qwZ INT8 block quantization: x (fp32/fp16/bf16, CUDA) -> (codes, scales)."""
     torch = _torch()
+    dev = _gpu(x, "x")
     n = x.numel()
     if out is None:
-        out = (torch.empty(n, dtype=torch.int8, device=x.device),
-               torch.empty(n // block if block > 0 else 0, dtype=torch.float32, device=x.device))
+        out = (torch.empty(n, dtype=torch.int8, device=dev),
+               torch.empty(_blocks(n, block), dtype=torch.float32, device=dev))
     codes, scales = out
-    _need(codes, torch.int8, n, "codes")
-    _need(scales, torch.float32, n // block, "scales")
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
+    _need(codes, torch.int8, n, "codes", dev)
+    _need(scales, torch.float32, _blocks(n, block), "scales", dev)
     rc = lib().zpq_quant_i8(_ptr(x), dtype_code(x.dtype), n, block, _ptr(codes), _ptr(scales),
-                            _stream(stream))
+                            _stream(stream, dev))
     _check(rc, "zpq_quant_i8")
     return codes, scales
 
@@ -131,17 +148,16 @@ def quant_i8(x, block=256, out=None, stream=None):
 def quant_i8_tensor(x, out=None, stream=None):
     """Non-blocked INT8 quantization, one scale for all of x -> (codes, scale[1])."""
     torch = _torch()
+    dev = _gpu(x, "x")
     n = x.numel()
     if out is None:
-        out = (torch.empty(n, dtype=torch.int8, device=x.device),
-               torch.empty(1, dtype=torch.float32, device=x.device))
+        out = (torch.empty(n, dtype=torch.int8, device=dev),
+               torch.empty(1, dtype=torch.float32, device=dev))
     codes, scale = out
-    _need(codes, torch.int8, n, "codes")
-    _need(scale, torch.float32, 1, "scale")
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
+    _need(codes, torch.int8, n, "codes", dev)
+    _need(scale, torch.float32, 1, "scale", dev)
     rc = lib().zpq_quant_i8_tensor(_ptr(x), dtype_code(x.dtype), n, _ptr(codes), _ptr(scale),
-                                   _stream(stream))
+                                   _stream(stream, dev))
     _check(rc, "zpq_quant_i8_tensor")
     return codes, scale
 
@@ -149,13 +165,15 @@ def quant_i8_tensor(x, out=None, stream=None):
 def dequant_i8(codes, scales, block=256, dtype=None, out=None, stream=None):
     """qwZ INT8 block dequantization: (codes, scales) -> y of `dtype`."""
     torch = _torch()
+    dev = _gpu(codes, "codes")
     n = codes.numel()
+    _need(codes, torch.int8, n, "codes", dev)
+    _need(scales, torch.float32, _blocks(n, block), "scales", dev)
     if out is None:
-        out = torch.empty(n, dtype=dtype or torch.float16, device=codes.device)
-    _need(codes, torch.int8, n, "codes")
-    _need(scales, torch.float32, n // block, "scales")
+        out = torch.empty(n, dtype=dtype or torch.float16, device=dev)
+    _need(out, out.dtype, n, "out", dev)
     rc = lib().zpq_dequant_i8(_ptr(codes), _ptr(scales), n, block, _ptr(out),
-                              dtype_code(out.dtype), _stream(stream))
+                              dtype_code(out.dtype), _stream(stream, dev))
     _check(rc, "zpq_dequant_i8")
     return out
 
@@ -163,47 +181,48 @@ def dequant_i8(codes, scales, block=256, dtype=None, out=None, stream=None):
 def qgz_reorder_quant_i4(grad, local_ranks, nodes, block=128, out=None, stream=None):
     """qgZ slice reorder + INT4 block quantization -> (codes [n/2], scales [n/block])."""
     torch = _torch()
+    dev = _gpu(grad, "grad")
     n = grad.numel()
     if out is None:
-        out = (torch.empty(n // 2, dtype=torch.uint8, device=grad.device),
-               torch.empty(n // block if block > 0 else 0, dtype=torch.float32, device=grad.device))
+        out = (torch.empty(n // 2, dtype=torch.uint8, device=dev),
+               torch.empty(_blocks(n, block), dtype=torch.float32, device=dev))
     codes, scales = out
-    _need(codes, torch.uint8, n // 2, "codes")
-    _need(scales, torch.float32, n // block, "scales")
-    if not grad.is_contiguous():
-        raise ValueError("grad must be contiguous")
+    _need(codes, torch.uint8, n // 2, "codes", dev)
+    _need(scales, torch.float32, _blocks(n, block), "scales", dev)
     rc = lib().zpq_qgz_reorder_quant_i4(_ptr(grad), dtype_code(grad.dtype), n, local_ranks, nodes,
-                                        block, _ptr(codes), _ptr(scales), _stream(stream))
+                                        block, _ptr(codes), _ptr(scales), _stream(stream, dev))
     _check(rc, "zpq_qgz_reorder_quant_i4")
     return codes, scales
 
 
 def qgz_dequant_reduce_requant_i4(in_codes, in_scales, n_src, chunk, block=128, out_dtype=None,
                                   divisor=1.0, out=None, stream=None):
-    """qgZ receive side of one all-to-all hop.  Hop 1 (out_dtype None):
-    -> (codes [chunk/2], scales [chunk/block]); hop 2: -> values [chunk]."""
+    """qgZ receive side of one all-to-all hop.  Hop 1 (out_dtype None and out
+    None or a (codes, scales) pair): -> (codes [chunk/2], scales [chunk/block]);
+    hop 2: -> values [chunk] of out_dtype (or of out's type)."""
     torch = _torch()
-    _need(in_codes, torch.uint8, n_src * (chunk // 2), "in_codes")
-    _need(in_scales, torch.float32, n_src * (chunk // block), "in_scales")
-    dev = in_codes.device
-    if out_dtype is None and not (out is not None and not isinstance(out, tuple)):
+    dev = _gpu(in_codes, "in_codes")
+    _need(in_codes, torch.uint8, n_src * (chunk // 2), "in_codes", dev)
+    _need(in_scales, torch.float32, n_src * _blocks(chunk, block), "in_scales", dev)
+    if out_dtype is None and (out is None or isinstance(out, tuple)):
         if out is None:
             out = (torch.empty(chunk // 2, dtype=torch.uint8, device=dev),
-                   torch.empty(chunk // block, dtype=torch.float32, device=dev))
+                   torch.empty(_blocks(chunk, block), dtype=torch.float32, device=dev))
         oc, os_ = out
-        _need(oc, torch.uint8, chunk // 2, "out_codes")
-        _need(os_, torch.float32, chunk // block, "out_scales")
+        _need(oc, torch.uint8, chunk // 2, "out_codes", dev)
+        _need(os_, torch.float32, _blocks(chunk, block), "out_scales", dev)
         rc = lib().zpq_qgz_dequant_reduce_requant_i4(
             _ptr(in_codes), _ptr(in_scales), n_src, chunk, block, _ptr(oc), _ptr(os_),
-            ctypes.c_void_p(0), 0, ctypes.c_float(1.0), _stream(stream))
+            ctypes.c_void_p(0), 0, ctypes.c_float(1.0), _stream(stream, dev))
         _check(rc, "zpq_qgz_dequant_reduce_requant_i4")
         return oc, os_
     if out is None:
         out = torch.empty(chunk, dtype=out_dtype, device=dev)
+    _need(out, out.dtype, chunk, "out", dev)
     rc = lib().zpq_qgz_dequant_reduce_requant_i4(
         _ptr(in_codes), _ptr(in_scales), n_src, chunk, block, ctypes.c_void_p(0),
         ctypes.c_void_p(0), _ptr(out), dtype_code(out.dtype), ctypes.c_float(divisor),
-        _stream(stream))
+        _stream(stream, dev))
     _check(rc, "zpq_qgz_dequant_reduce_requant_i4")
     return out
 

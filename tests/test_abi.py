@@ -170,3 +170,21 @@ def test_bench_measures_one_gpu_only():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes raw pointers: tensors not on a GPU are refused in
+    Python, before the library sees them."""
+    import torch
+    x = torch.zeros(1024, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        zpq.quant_i8(x, 256)
+    with pytest.raises(ValueError):
+        zpq.quant_i8_tensor(x)
+    with pytest.raises(ValueError):
+        zpq.qgz_reorder_quant_i4(x, 2, 2, 64)
+    with pytest.raises(ValueError):
+        zpq.dequant_i8(torch.zeros(1024, dtype=torch.int8), torch.zeros(4), 256)
+    with pytest.raises(ValueError):
+        zpq.qgz_dequant_reduce_requant_i4(torch.zeros(1024, dtype=torch.uint8),
+                                           torch.zeros(16), 2, 1024, 128)
