@@ -90,6 +90,19 @@
 #ifndef ZPQ_PERSIST_REDUCE
 #define ZPQ_PERSIST_REDUCE 0
 #endif
+// Give each XCD a contiguous range of tiles, per kernel.
+#ifndef ZPQ_XCD_QUANT
+#define ZPQ_XCD_QUANT 0
+#endif
+#ifndef ZPQ_XCD_DEQUANT
+#define ZPQ_XCD_DEQUANT 1
+#endif
+#ifndef ZPQ_XCD_QGZ
+#define ZPQ_XCD_QGZ 0
+#endif
+#ifndef ZPQ_XCD_REDUCE
+#define ZPQ_XCD_REDUCE 0
+#endif
 #ifndef ZPQ_THREADS
 #define ZPQ_THREADS 256
 #endif
@@ -140,6 +153,19 @@ __device__ __forceinline__ void st_stream(T v, T* p) {
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Tile processed by workgroup k of n.  Workgroups are dispatched round-robin
+// over the 8 XCDs (k mod 8); with the remap XCD x takes the contiguous tiles
+// [x*q + min(x, r), ...) where n = 8q + r: a bijection on [0, n).
+template <bool REMAP>
+__device__ __forceinline__ uint32_t tile_of(uint32_t k, uint32_t n) {
+    if constexpr (REMAP) {
+        const uint32_t x = k & 7u, i = k >> 3, q = n >> 3, r = n & 7u;
+        return x * q + (x < r ? x : r) + i;
+    } else {
+        return k;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Cross-lane maximum over aligned groups of G lanes (G = 1, 2, 4, ..., 32).
@@ -378,7 +404,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_i8(const void* __restrict__ 
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales, uint32_t nvb) {
     constexpr int G = BLOCK / EPL;
-    for (uint32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+    for (uint32_t k = blockIdx.x; k < nvb; k += gridDim.x) {
+    const uint32_t vb = tile_of<ZPQ_XCD_QUANT>(k, nvb);
     const int64_t wg_base = (int64_t)vb * (U * kThreads * EPL);
     InTile<DT, EPL> tile[U];
 #pragma unroll
@@ -557,7 +584,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_i8(const int8_t* __restric
                                                          uint32_t nvb) {
     static_assert((EPL == 8 || EPL % 16 == 0) && EPL <= BLOCK, "code vectors inside a block");
     constexpr int V = EPL >= 16 ? EPL / 16 : 1;
-    for (uint32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+    for (uint32_t k = blockIdx.x; k < nvb; k += gridDim.x) {
+    const uint32_t vb = tile_of<ZPQ_XCD_DEQUANT>(k, nvb);
     const int64_t wg_base = (int64_t)vb * (U * kThreads * EPL);
     u32x4 cw[U][V];
     float s[U];
@@ -604,7 +632,8 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
     const void* __restrict__ grad, int64_t S, int32_t L, int32_t N, uint32_t wgs_per_slice,
     uint8_t* __restrict__ codes, float* __restrict__ scales, uint32_t nvb) {
     constexpr int G = BLOCK / EPL;
-    for (uint32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+    for (uint32_t k = blockIdx.x; k < nvb; k += gridDim.x) {
+    const uint32_t vb = tile_of<ZPQ_XCD_QGZ>(k, nvb);
     const uint32_t p = vb / wgs_per_slice;
     const uint32_t w = vb - p * wgs_per_slice;
     const uint32_t j = p / (uint32_t)N;
@@ -763,7 +792,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
     void* __restrict__ out_vals, float divisor, float rdiv, bool div_fast, uint32_t nvb) {
-    for (uint32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+    for (uint32_t k = blockIdx.x; k < nvb; k += gridDim.x) {
+    const uint32_t vb = tile_of<ZPQ_XCD_REDUCE>(k, nvb);
         const int64_t e = ((int64_t)vb * kThreads + threadIdx.x) * EPL;
         if (e < c)                 // whole quantization blocks leave together
             reduce_tile<BLOCK, EPL, OUT, PF>(in_codes, in_scales, K, c, out_codes, out_scales,
