@@ -302,3 +302,53 @@ def test_quant_i8_tensor(dtype, kind):
         rc, rs = oracle.quant_i8(xs, dtype, n)
         assert_bits_equal(from_device(scale), rs, "scale")
         assert_bits_equal(from_device(codes), rc, "codes")
+
+
+def boundary_blocks(dtype, qmax, B):
+    """One block per positive finite 16-bit absmax a (sign alternating by
+    block): a itself, then for each k < qmax the two values of the type on
+    either side of the rounding boundary (k + 1/2) * fl32(a / qmax), clipped to
+    a; zero padding.  Returns the blocks as 16-bit patterns."""
+    import torch
+    top = 0x7F80 if dtype == "bf16" else 0x7C00
+    a_bits = np.arange(1, top, dtype=np.uint32).astype(np.uint16)
+    a32 = oracle.bf16_to_f32(a_bits) if dtype == "bf16" else a_bits.view(np.float16).astype(np.float32)
+    s = (a32 / np.float32(qmax)).astype(np.float32)
+    k = np.arange(qmax, dtype=np.float64)
+    t = (k[None, :] + 0.5) * s[:, None].astype(np.float64)          # [A, qmax]
+    tt = torch.from_numpy(t.astype(np.float32).ravel())
+    if dtype == "bf16":
+        near = tt.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    else:
+        near = tt.to(torch.float16).numpy().view(np.uint16)
+    near = near.reshape(t.shape).astype(np.int32)
+    cand = np.stack([near - 1, near, near + 1], axis=2).reshape(len(a_bits), -1)
+    cand = np.clip(cand, 0, a_bits.astype(np.int32)[:, None])          # |x| <= a
+    need = 1 + cand.shape[1]
+    assert need <= B, (need, B)
+    blocks = np.zeros((len(a_bits), B), np.uint16)
+    blocks[:, 0] = a_bits
+    blocks[:, 1:need] = cand.astype(np.uint16)
+    blocks[1::2] |= np.uint16(0x8000)                                    # negative blocks
+    blocks[1::2][blocks[1::2] == 0x8000] = 0                             # no -0 padding
+    return blocks.ravel()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_rounding_boundaries_every_absmax(dtype):
+    """The inputs where a quotient off by one ulp would change a code: for
+    every 16-bit absmax, the values next to each rounding boundary, through
+    the INT8 quantizer (qmax 127) and the INT4 quantizer (qmax 7)."""
+    for qmax, B in ((127, 512), (7, 32)):
+        bits = boundary_blocks(dtype, qmax, B)
+        x = bits if dtype == "bf16" else bits.view(np.float16)
+        print(f"rounding boundaries dtype={dtype} qmax={qmax} n={bits.size}", flush=True)
+        xd = to_device(x, dtype)
+        if qmax == 127:
+            codes, scales = zpq.quant_i8(xd, B)
+            rc, rs = oracle.quant_i8(x, dtype, B)
+        else:
+            codes, scales = zpq.qgz_reorder_quant_i4(xd, 1, 1, B)
+            rc, rs = oracle.qgz_reorder_quant_i4(x, dtype, 1, 1, B)
+        assert_bits_equal(from_device(scales), rs, "scales")
+        assert_bits_equal(from_device(codes), rc, "codes")
