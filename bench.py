@@ -370,7 +370,7 @@ def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):
             "error": "RMS(y - exact mean) / RMS(exact mean), fp64 reference"}
 
 
-def per_config(np, torch, zpq, synth, reps=30, settle_s=0.2):
+def per_config(np, torch, zpq, synth, reps=50, settle_s=0.2):
     """Every kernel at every workload size, one launch at a time: before each
     timed launch a read-only pass over 1 GiB of scratch evicts the 256 MB
     last-level cache (reads leave no dirty lines behind to be written back
