@@ -352,3 +352,37 @@ def test_rounding_boundaries_every_absmax(dtype):
             rc, rs = oracle.qgz_reorder_quant_i4(x, dtype, 1, 1, B)
         assert_bits_equal(from_device(scales), rs, "scales")
         assert_bits_equal(from_device(codes), rc, "codes")
+
+
+def test_explicit_side_stream():
+    """Every entry point enqueues on the stream it is given: the whole chain
+    on a side stream (default priority), then one synchronize, equals the
+    oracle."""
+    import torch
+    rng = np.random.default_rng(91)
+    s = torch.cuda.Stream()
+    n, B, L, N = 8 * 4096, 128, 2, 2
+    x = as_dtype((rng.standard_normal(n) * 0.02).astype(np.float32), "bf16")
+    xd = to_device(x, "bf16")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c8, s8 = zpq.quant_i8(xd, B, stream=s)
+        y8 = zpq.dequant_i8(c8, s8, B, torch.bfloat16, stream=s)
+        ct, st_ = zpq.quant_i8_tensor(xd, stream=s)
+        c4, s4 = zpq.qgz_reorder_quant_i4(xd, L, N, B, stream=s)
+        c5, s5 = zpq.qgz_dequant_reduce_requant_i4(c4, s4, L, n // L, B, stream=s)
+        y5 = zpq.qgz_dequant_reduce_requant_i4(c5, s5, N, n // (L * N), B, out_dtype=torch.float32,
+                                                divisor=4.0, stream=s)
+    s.synchronize()
+    rc8, rs8 = oracle.quant_i8(x, "bf16", B)
+    assert_bits_equal(from_device(c8), rc8, "codes")
+    assert_bits_equal(from_device(y8), oracle.dequant_i8(rc8, rs8, B, "bf16"), "dequant")
+    rct, rst = oracle.quant_i8(x, "bf16", n)
+    assert_bits_equal(from_device(ct), rct, "per-tensor codes")
+    assert_bits_equal(from_device(st_), rst, "per-tensor scale")
+    rc4, rs4 = oracle.qgz_reorder_quant_i4(x, "bf16", L, N, B)
+    assert_bits_equal(from_device(c4), rc4, "INT4 codes")
+    rc5, rs5 = oracle.qgz_dequant_reduce_requant_i4(rc4, rs4, L, n // L, B)
+    assert_bits_equal(from_device(c5), rc5, "hop-1 codes")
+    ry = oracle.qgz_dequant_reduce_requant_i4(rc5, rs5, N, n // (L * N), B, "f32", 4.0)
+    assert_bits_equal(from_device(y5), ry, "hop-2 values")
