@@ -127,7 +127,8 @@ def test_dequant_reduce_requant_i4(block, K):
 @pytest.mark.parametrize("out", DTYPES)
 @pytest.mark.parametrize("block", [32, 64, 128, 512])
 @pytest.mark.parametrize("K,divisor", [(1, 1.0), (3, 3.0), (16, 16.0), (48, 384.0),
-                                       (8, 0.5), (5, 2.0 ** 50), (4, 1e-30)])
+                                       (8, 0.5), (5, 2.0 ** 50), (4, 1e-30), (3, 2.0 ** -126),
+                                       (2, 2.0 ** 126), (2, 2.0 ** 127)])
 def test_dequant_reduce_average(out, block, K, divisor):
     rng = np.random.default_rng(block + K)
     chunk = (256 * 16 // block * 2 + 3) * block
