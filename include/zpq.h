@@ -32,7 +32,9 @@
  *   - Element counts are 64-bit, at most 2^40 (else ZPQ_ERR_SIZE); buffers
  *     above 2^31 bytes are supported.
  *   - ZPQ_ERR_LAUNCH reports a launch failure from the HIP runtime (for
- *     example a device other than gfx950).
+ *     example a device other than gfx950), read with hipGetLastError after
+ *     the launches: an error left pending by an earlier HIP call on the same
+ *     host thread is reported (and cleared) the same way.
  *   - Calls that write the same output concurrently race; calls on one
  *     stream are ordered.
  */
