@@ -38,7 +38,8 @@
  *   O7 reorder      zpq_ref_reorder
  *   O8 reduce       zpq_ref_reduce_add
  *   O9 average      zpq_ref_average
- * and four compositions that mirror the four libzpq entry points.
+ * and four compositions that mirror libzpq's entry points (its per-tensor
+ * quantizer is zpq_ref_quant_i8 with a single block spanning the tensor).
  */
 #include <math.h>
 #include <stdint.h>
