@@ -188,8 +188,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
-    per_kernel_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in sampled]))
-                     for i in range(len(kernels))]
+    samples_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in sampled]
+                  for i in range(len(kernels))]
+    per_kernel_ms = [float(np.mean(v)) for v in samples_ms]
 
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -212,9 +213,11 @@ def main():
                 traffic = t.get("bytes_per_launch", {})
 
     rows = []
-    for (name, _, nbytes), ms in zip(kernels, per_kernel_ms):
+    for (name, _, nbytes), ms, smp in zip(kernels, per_kernel_ms, samples_ms):
         gbs = nbytes / (ms * 1e-3) / 1e9
         rows.append({"kernel": name, "bytes": nbytes, "us": round(ms * 1e3, 2),
+                     "us_median": round(float(np.median(smp)) * 1e3, 2),
+                     "us_min": round(float(np.min(smp)) * 1e3, 2),
                      "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
     dom = max(range(len(rows)), key=lambda i: per_kernel_ms[i])
     dk = rows[dom]
