@@ -57,7 +57,10 @@ def parse():
                          "size, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-kernel HBM bytes from rocprofv3 counters (optional)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
+    return args
 
 
 def main():
