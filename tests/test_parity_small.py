@@ -107,7 +107,7 @@ def random_received(rng, K, chunk, block, huge=False):
 
 
 @pytest.mark.parametrize("block", BLOCKS)
-@pytest.mark.parametrize("K", [1, 2, 3, 5, 8, 16, 48])
+@pytest.mark.parametrize("K", [1, 2, 3, 5, 8, 16, 48, 97])
 def test_dequant_reduce_requant_i4(block, K):
     rng = np.random.default_rng(block * 100 + K)
     chunk = (256 * 16 // block * 3 + 1) * block               # several tiles + ragged
@@ -128,7 +128,7 @@ def test_dequant_reduce_requant_i4(block, K):
 @pytest.mark.parametrize("block", [32, 64, 128, 512])
 @pytest.mark.parametrize("K,divisor", [(1, 1.0), (3, 3.0), (16, 16.0), (48, 384.0),
                                        (8, 0.5), (5, 2.0 ** 50), (4, 1e-30), (3, 2.0 ** -126),
-                                       (2, 2.0 ** 126), (2, 2.0 ** 127)])
+                                       (2, 2.0 ** 126), (2, 2.0 ** 127), (97, 97.0)])
 def test_dequant_reduce_average(out, block, K, divisor):
     rng = np.random.default_rng(block + K)
     chunk = (256 * 16 // block * 2 + 3) * block
