@@ -59,13 +59,13 @@
 #define ZPQ_QGZ_U 2            // tiles per lane, reorder + INT4 quantize
 #endif
 #ifndef ZPQ_REDUCE_EPL_I4
-#define ZPQ_REDUCE_EPL_I4 16   // elements per lane, hop-1 receive (INT4 out)
+#define ZPQ_REDUCE_EPL_I4 32   // elements per lane, hop-1 receive (INT4 out)
 #endif
 #ifndef ZPQ_REDUCE_EPL_FL
 #define ZPQ_REDUCE_EPL_FL 16   // elements per lane, hop-2 receive (float out)
 #endif
 #ifndef ZPQ_REDUCE_PF_I4
-#define ZPQ_REDUCE_PF_I4 4     // received sources in flight per lane (hop 1)
+#define ZPQ_REDUCE_PF_I4 2     // received sources in flight per lane (hop 1)
 #endif
 #ifndef ZPQ_REDUCE_PF_FL
 #define ZPQ_REDUCE_PF_FL 2     // received sources in flight per lane (hop 2)
