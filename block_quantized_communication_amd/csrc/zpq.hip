@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -153,6 +154,9 @@ __device__ __forceinline__ void st_stream(T v, T* p) {
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Tile processed by workgroup k of n.  Workgroups are dispatched round-robin
 // over the 8 XCDs (k mod 8); with the remap XCD x takes the contiguous tiles
@@ -191,20 +195,21 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// Correctly rounded division fl32(x / s), given r = fl32(1 / s).
-// q0 = x*r is within 1.5 ulp of x/s; one residual step (the residual
-// x - q*s is exact in an FMA) brings it within 1 ulp; a second step then
-// returns the correctly rounded quotient (Markstein's theorem, see Muller et
-// al., Handbook of Floating-Point Arithmetic, division with an FMA).
-// Preconditions, checked by the callers: 2^-100 <= s (so 1/s is finite and
-// no residual underflows while |x/s| >= 1/4; smaller quotients only need to
-// stay below 1/2, which they do) and s <= 2^126.
-__device__ __forceinline__ float div_cr(float x, float s, float r) {
-    float q = x * r;
-    float e = __builtin_fmaf(-q, s, x);
-    q = __builtin_fmaf(e, r, q);
-    e = __builtin_fmaf(-q, s, x);
-    return __builtin_fmaf(e, r, q);
+// fl32(x / d) for binary32 x and d > 0, through binary64.  rd = RN64(1/d) is
+// within 2^-53 (relatively) of 1/d, so the binary64 product x * rd is within
+// 2^-52 of x / d.  A binary32 rounding boundary (a midpoint m between two
+// binary32 numbers, 25 significant bits) cannot be closer than 2^-49
+// (relatively) to a quotient x / d of binary32 numbers that is itself in the
+// normal binary32 range: x - m*d is a nonzero multiple of ulp(m)*ulp(d)/2 (the
+// odd part of m*d has at least 25 bits, x at most 24, so they differ).  The
+// product therefore lies on the same side of every boundary as x / d, and one
+// rounding to binary32 gives the IEEE quotient (the double-rounding argument of
+// Figueroa, 1995, with the product's error in place of the first rounding).
+// Quotients below 2^-126 are not covered (the boundaries of the subnormal
+// grid can be hit exactly); callers route those elsewhere or do not depend
+// on them.
+__device__ __forceinline__ float div_f64(float x, double rd) {
+    return (float)((double)x * rd);
 }
 
 // Round-half-even to integer and clamp to [-QMAX, QMAX]; the integer lands in
@@ -233,28 +238,40 @@ __device__ __forceinline__ uint32_t round_code_fast(float t) {
     return __float_as_uint(t + 12582912.0f);
 }
 
-// Codes of N values given the final scale s.  Fast path (s >= 2^-100):
-// ONE_STEP (16-bit inputs) takes one residual correction with any r within
-// one ulp of 1/s; otherwise two corrections with r = fl32(1/s).  The slow
-// path (tiny or zero scale, block-uniform) divides with the IEEE operator.
-template <int QMAX, bool ONE_STEP, int N>
-__device__ __forceinline__ void codes_of(float s, float r, bool fast, const float (&v)[N],
-                                         uint32_t (&out)[N]) {
+// Codes of N values for a known scale s, as rounded bit patterns.
+//  16-bit inputs: fast when s >= 2^-100, with r within one ulp of 1/s
+//  (div_1c, exhaustively checked); otherwise the IEEE operator, clamped
+//  (s == 0 gives codes 0).
+template <int QMAX, int N>
+__device__ __forceinline__ void codes16(float s, float r, bool fast, const float (&v)[N],
+                                        uint32_t (&out)[N]) {
     if (fast) {
 #pragma unroll
-        for (int k = 0; k < N; ++k)
-            out[k] = round_code_fast(ONE_STEP ? div_1c(v[k], s, r) : div_cr(v[k], s, r));
+        for (int k = 0; k < N; ++k) out[k] = round_code_fast(div_1c(v[k], s, r));
     } else {
 #pragma unroll
         for (int k = 0; k < N; ++k) out[k] = round_code<QMAX>(s != 0.0f ? v[k] / s : 0.0f);
     }
 }
 
+//  fp32 values: rd = RN64(1/s) (0 when s == 0); the code is rint(div_f64(x, rd)),
+//  exact for every s > 0: a quotient below 2^-126, which div_f64 does not
+//  cover, is below 1/2 and gives code 0 either way.  normal = (s >= 2^-126):
+//  then no code exceeds QMAX and the clamp is skipped.
+template <int QMAX, int N>
+__device__ __forceinline__ void codes32(double rd, bool normal, const float (&v)[N],
+                                        uint32_t (&out)[N]) {
+    if (normal) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) out[k] = round_code_fast(div_f64(v[k], rd));
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) out[k] = round_code<QMAX>(div_f64(v[k], rd));
+    }
+}
+
 // Per-block quantizer state from the block absmax a: scale s = fl32(a / QMAX)
-// and, on the fast path, a reciprocal r.
-//  * fp32 inputs (ONE_STEP false): s by the corrected division by the
-//    constant QMAX (exact for a >= 2^-90, where no residual underflows), else
-//    the IEEE operator; fast when s >= 2^-100, with r = fl32(1/s).
+// and a reciprocal for the codes.
 //  * 16-bit inputs (ONE_STEP true), branch-free: s = fl32(a * k) plus one
 //    residual correction (k = fl32(1/QMAX)), and r = the hardware reciprocal
 //    of s refined by one Newton step, which leaves r within one ulp of 1/s.
@@ -262,10 +279,16 @@ __device__ __forceinline__ void codes_of(float s, float r, bool fast, const floa
 //    fl32(a / QMAX), and div_1c with either float next to 1/s gives the IEEE
 //    codes: both checked by exhaustion over all (a, x) pairs of both types
 //    and both QMAX.  fast = (a >= 2^-90); a slower block's exact scale
-//    a / QMAX (possibly subnormal) is computed by codes(), on its slow path.
+//    a / QMAX (possibly subnormal) is computed on its slow path.
+//  * fp32 inputs (ONE_STEP false): s = div_f64(a, RN64(1/QMAX)) when a/QMAX is
+//    a normal binary32 number (a >= 2^-118), else the IEEE operator; then
+//    rd = RN64(1/s) (0 for s == 0) and every code is rint(div_f64(x, rd)),
+//    exact for any s > 0 (a quotient too small for div_f64 rounds to code 0
+//    either way).  The clamp is needed only when s is subnormal.
 template <int QMAX, bool ONE_STEP>
 struct BlockScale {
     float a, s, r;
+    double rd;
     bool fast;
     BlockScale() = default;
     __device__ __forceinline__ explicit BlockScale(float a_) : a(a_) {
@@ -278,21 +301,21 @@ struct BlockScale {
             r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
             fast = a >= 0x1p-90f;
         } else {
-            if (a >= 0x1p-90f) s = div_cr(a, kQ, kInvQ);
-            else s = a / kQ;
-            fast = s >= 0x1p-100f;
-            r = fast ? 1.0f / s : 0.0f;
+            constexpr double kInvQ64 = 1.0 / (double)QMAX;
+            s = a >= 0x1p-118f ? div_f64(a, kInvQ64) : a / kQ;
+            rd = s > 0.0f ? 1.0 / (double)s : 0.0;
+            fast = s >= 0x1p-126f;
         }
     }
     // Codes of N values (as rounded bit patterns); afterwards s is the
     // block's scale on every path.
     template <int N>
     __device__ __forceinline__ void codes(const float (&v)[N], uint32_t (&out)[N]) {
-        if (fast) {
-            codes_of<QMAX, ONE_STEP>(s, r, true, v, out);
+        if constexpr (ONE_STEP) {
+            if (!fast) s = a / (float)QMAX;
+            codes16<QMAX>(s, r, fast, v, out);
         } else {
-            if constexpr (ONE_STEP) s = a / (float)QMAX;
-            codes_of<QMAX, ONE_STEP>(s, r, false, v, out);
+            codes32<QMAX>(rd, fast, v, out);
         }
     }
 };
@@ -510,12 +533,15 @@ __global__ __launch_bounds__(kThreads) void k_tensor_scale(const uint32_t* __res
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_tensor_codes(const void* __restrict__ x, int64_t n,
                                                            const float* __restrict__ scale,
-                                                           int8_t* __restrict__ codes) {
+                                                           int8_t* __restrict__ codes,
+                                                           uint32_t nvb) {
     constexpr int EPL = kTensorEpl;
     const float s = scale[0];
-    const bool fast = s >= 0x1p-100f;
-    const float r = fast ? 1.0f / s : 0.0f;
-    const int64_t base = (int64_t)blockIdx.x * kTensorTile;
+    const bool fast16 = s >= 0x1p-100f;
+    const float r = fast16 ? 1.0f / s : 0.0f;
+    const double rd = s > 0.0f ? 1.0 / (double)s : 0.0;
+    for (uint32_t t = blockIdx.x; t < nvb; t += gridDim.x) {
+    const int64_t base = (int64_t)t * kTensorTile;
     InTile<DT, EPL> tile[kTensorU];
 #pragma unroll
     for (int u = 0; u < kTensorU; ++u) {
@@ -529,11 +555,13 @@ __global__ __launch_bounds__(kThreads) void k_tensor_codes(const void* __restric
 #pragma unroll
         for (int k = 0; k < EPL; ++k) v[k] = tile[u].get(k);
         uint32_t q[EPL];
-        codes_of<127, DT != ZPQ_F32>(s, r, fast, v, q);
+        if constexpr (DT == ZPQ_F32) codes32<127>(rd, s >= 0x1p-126f, v, q);
+        else codes16<127>(s, r, fast16, v, q);
         if (e < n)
             st_stream<false>(u32x2{pack_low_bytes(q[0], q[1], q[2], q[3]),
                                    pack_low_bytes(q[4], q[5], q[6], q[7])},
                              reinterpret_cast<u32x2*>(codes + e));
+    }
     }
 }
 
@@ -555,19 +583,15 @@ __device__ __forceinline__ void store_out(void* __restrict__ y, int64_t e, const
         for (int k = 0; k < EPL / 2; ++k) {
             // The fp32 value must be rounded to fp32 first and then to the
             // 16-bit type.  The empty asm keeps the compiler from fusing the
-            // producing multiply into a mixed-precision FMA (v_fma_mixlo_f16
+            // producing operation into a mixed-precision FMA (v_fma_mixlo_f16
             // with a +0 addend), which rounds once and loses the sign of zero.
-            float a = v[2 * k], b = v[2 * k + 1];
-            asm("" : "+v"(a), "+v"(b));
-            uint32_t lo, hi;
-            if constexpr (OT == ZPQ_F16) {
-                lo = __half_as_ushort(__float2half_rn(a));
-                hi = __half_as_ushort(__float2half_rn(b));
-            } else {
-                lo = __bfloat16_as_ushort(__float2bfloat16(a));
-                hi = __bfloat16_as_ushort(__float2bfloat16(b));
-            }
-            h[k] = lo | (hi << 16);
+            // One v_cvt_pk_{f16,bf16}_f32 rounds both values to nearest even.
+            f32x2 ab = {v[2 * k], v[2 * k + 1]};
+            asm("" : "+v"(ab));
+            if constexpr (OT == ZPQ_F16)
+                h[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(ab, f16x2));
+            else
+                h[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(ab, bf16x2));
         }
         u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + e);
 #pragma unroll
@@ -679,11 +703,14 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
 // Per source and element: d = fl32(q * s) computed as fma(u, s, -8s) with
 // u = q + 8 in 0..15 (the nibble with its top bit flipped, converted by
 // v_cvt_f32_ubyte): the FMA rounds the exact (u - 8) * s once, which is
-// fl32(q * s).  -8s is exact unless 8|s| overflows; then that source's terms
-// are -inf and the lane's sums end non-finite, which the lane checks once at
-// the end and answers by recomputing with q * s directly (the recomputation
-// is the definition itself, so it is also right when a true sum overflows).
-// The sum is acc = fl32(acc + d), starting at +0, sources in order 0..K-1.
+// fl32(q * s).  -8s is exact unless 8|s| overflows (|s| > FLT_MAX/8); then that
+// source's terms are -inf, and since all elements of a lane share each
+// source's scale, every sum of the lane ends -inf or NaN (no term is ever
+// +inf: a valid -8s keeps |(u - 8) * s| <= 8|s| finite).  The lane therefore
+// checks one sum at the end and, if it is not finite, recomputes with q * s
+// directly, which is the definition itself and so also right when true sums
+// overflow.  The sum is acc = fl32(acc + d), starting at +0, sources in order
+// 0..K-1.
 template <int EPL>
 struct SrcCodes {
     static constexpr int W = EPL / 8;     // dwords of nibbles per lane and source
@@ -760,13 +787,35 @@ __device__ __forceinline__ void accumulate(float (&acc)[EPL], const SrcCodes<EPL
     }
 }
 
-// max(m, |a|, |b|) in one v_max3_f32 with |.| source modifiers.  Written as
-// asm: the compiler would otherwise canonicalize each loop-carried operand
-// first (an extra instruction per element).
+// max(m, |a|, |b|) and min(m, |a|, |b|) in one v_max3_f32 / v_min3_f32 with
+// |.| source modifiers.  Written as asm: the compiler would otherwise
+// canonicalize each loop-carried operand first (an extra instruction per
+// element).  Quiet NaN operands are ignored (IEEE mode), which the callers
+// allow for.
 __device__ __forceinline__ float max3_abs(float m, float a, float b) {
     float r;
     asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(m));
     return r;
+}
+__device__ __forceinline__ float min3_abs(float m, float a, float b) {
+    float r;
+    asm("v_min3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(m));
+    return r;
+}
+
+// max |v| (mx) or min |v| over N values, in two independent chains so that
+// consecutive instructions do not wait on each other.
+template <bool MAX, int N>
+__device__ __forceinline__ float reduce_abs(const float (&v)[N]) {
+    static_assert(N % 2 == 0, "pairs");
+    float m0 = MAX ? 0.0f : __builtin_inff(), m1 = m0;
+#pragma unroll
+    for (int k = 0; k < N; k += 4) {
+        m0 = MAX ? max3_abs(m0, v[k], v[k + 1]) : min3_abs(m0, v[k], v[k + 1]);
+        if (k + 3 < N)
+            m1 = MAX ? max3_abs(m1, v[k + 2], v[k + 3]) : min3_abs(m1, v[k + 2], v[k + 3]);
+    }
+    return MAX ? fmaxf(m0, m1) : fminf(m0, m1);
 }
 
 template <int EPL>
@@ -785,19 +834,19 @@ template <int BLOCK, int EPL, int OUT, int PF>
 __device__ __forceinline__ void reduce_tile(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
-    void* __restrict__ out_vals, float divisor, float rdiv, bool div_fast, int64_t e);
+    void* __restrict__ out_vals, float divisor, double rdiv, float thr, int64_t e);
 
 template <int BLOCK, int EPL, int OUT /* -1: INT4, else a zpq_dtype */, int PF>
 __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
-    void* __restrict__ out_vals, float divisor, float rdiv, bool div_fast, uint32_t nvb) {
+    void* __restrict__ out_vals, float divisor, double rdiv, float thr, uint32_t nvb) {
     for (uint32_t k = blockIdx.x; k < nvb; k += gridDim.x) {
     const uint32_t vb = tile_of<ZPQ_XCD_REDUCE>(k, nvb);
         const int64_t e = ((int64_t)vb * kThreads + threadIdx.x) * EPL;
         if (e < c)                 // whole quantization blocks leave together
             reduce_tile<BLOCK, EPL, OUT, PF>(in_codes, in_scales, K, c, out_codes, out_scales,
-                                             out_vals, divisor, rdiv, div_fast, e);
+                                             out_vals, divisor, rdiv, thr, e);
     }
 }
 
@@ -805,7 +854,7 @@ template <int BLOCK, int EPL, int OUT, int PF>
 __device__ __forceinline__ void reduce_tile(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
-    void* __restrict__ out_vals, float divisor, float rdiv, bool div_fast, int64_t e) {
+    void* __restrict__ out_vals, float divisor, double rdiv, float thr, int64_t e) {
     constexpr int G = BLOCK / EPL;
     const int64_t cstride = c / 2, sstride = c / BLOCK;
     const uint32_t coff = (uint32_t)(e / 2), soff = (uint32_t)(e / BLOCK);   // c < 2^32
@@ -848,14 +897,9 @@ __device__ __forceinline__ void reduce_tile(
             accumulate<EPL>(acc, d);
         }
     }
-    // max |acc| (v_max3_f32 with |.| modifiers).  An overflowed -8s makes the
-    // lane's sums -inf, which this maximum exposes; a NaN sum would need a
-    // true partial sum that already overflowed (outside the domain).
-    float m = 0.0f;
-#pragma unroll
-    for (int k = 0; k < EPL; k += 2) m = max3_abs(m, acc[k], acc[k + 1]);
-    if (!(m <= 3.4028234663852886e38f)) {
-        // a non-finite sum: redo this lane with q * s directly
+    // An overflowed -8s leaves every sum of the lane -inf or NaN (see above):
+    // one sum decides whether the lane is recomputed with q * s directly.
+    if (!(fabsf(acc[0]) <= 3.4028234663852886e38f)) {
 #pragma unroll
         for (int k = 0; k < EPL; ++k) acc[k] = 0.0f;
         for (int i = 0; i < K; ++i) {
@@ -863,38 +907,41 @@ __device__ __forceinline__ void reduce_tile(
             src_load(d, i);
             accumulate_direct<EPL>(acc, d);
         }
-        m = 0.0f;
-#pragma unroll
-        for (int k = 0; k < EPL; k += 2) m = max3_abs(m, acc[k], acc[k + 1]);
     }
-    const uint32_t mbits = __float_as_uint(m);
 
     if constexpr (OUT < 0) {
-        const float a = __uint_as_float(group_max<G>(mbits));
+        // Requantize the sums (sums that are not finite lie outside the
+        // quantizer's domain: their block's output is unspecified).
+        const float m = reduce_abs<true>(acc);
+        const float a = __uint_as_float(group_max<G>(__float_as_uint(m)));
         BlockScale<7, false> bs(a);
-        uint32_t q[EPL];
-        bs.codes(acc, q);
         uint32_t packed[EPL / 8];
 #pragma unroll
-        for (int k = 0; k < EPL / 8; ++k) packed[k] = pack_nibbles(q + 8 * k);
+        for (int k = 0; k < EPL / 8; ++k) {       // 8 codes at a time: few live registers
+            float v[8];
+            uint32_t q[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = acc[8 * k + j];
+            bs.codes(v, q);
+            packed[k] = pack_nibbles(q);
+        }
         store_nibbles<EPL, ZPQ_NTS_REDUCE>(out_codes + e / 2, packed);
         if ((threadIdx.x & (G - 1)) == 0) out_scales[e / BLOCK] = bs.s;
     } else {
-        // y = fl32(acc / divisor): div_cr is exact when the divisor is in
-        // [1, 2^40] (checked on the host: the quotient cannot overflow) and
-        // |acc| >= 2^-60 or acc == 0 (the quotient is normal and no residual
-        // underflows); otherwise the IEEE operator.
-        bool fast = div_fast && m <= 3.4028234663852886e38f;
-#pragma unroll
-        for (int k = 0; k < EPL; ++k)
-            fast = fast && (fabsf(acc[k]) >= 0x1p-60f || acc[k] == 0.0f);
+        // y = fl32(acc / divisor) = div_f64(acc, RN64(1/divisor)) whenever the
+        // quotient is a normal binary32 number or overflows, i.e. for
+        // |acc| >= thr = 2^-126 * divisor (rounded up; set on the host), and
+        // for acc == 0, infinities and NaN.  A lane with a smaller nonzero sum
+        // divides those with the IEEE operator.
         float y[EPL];
-        if (fast) {
+        if (reduce_abs<false>(acc) >= thr) {
 #pragma unroll
-            for (int k = 0; k < EPL; ++k) y[k] = div_cr(acc[k], divisor, rdiv);
+            for (int k = 0; k < EPL; ++k) y[k] = div_f64(acc[k], rdiv);
         } else {
 #pragma unroll
-            for (int k = 0; k < EPL; ++k) y[k] = acc[k] / divisor;
+            for (int k = 0; k < EPL; ++k)
+                y[k] = (fabsf(acc[k]) >= thr || acc[k] == 0.0f) ? div_f64(acc[k], rdiv)
+                                                                 : acc[k] / divisor;
         }
         store_out<OUT, EPL, ZPQ_NTS_REDUCE>(out_vals, e, y);
     }
@@ -947,12 +994,18 @@ inline int cu_count() {
 // within 32 bits and byte counts within 64.
 constexpr int64_t kMaxElems = 1LL << 40;
 
-// Launch grid for nvb virtual blocks: all of them, or a persistent grid of
-// per_cu workgroups per compute unit that loops over them.
-inline unsigned launch_grid(unsigned nvb, int per_cu) {
-    if (per_cu <= 0) return nvb;
-    const int64_t g = (int64_t)per_cu * cu_count();
-    return (unsigned)(g < (int64_t)nvb ? g : (int64_t)nvb);
+// A dispatch holds at most 2^32 - 1 work-items per dimension, so at most
+// kMaxGrid workgroups; every kernel loops over its virtual blocks with a
+// stride of the grid size, so a capped grid still covers them all.
+constexpr unsigned kMaxGrid = 0xFFFFFFFFu / kThreads;
+
+// Launch grid for nvb virtual blocks: all of them (up to kMaxGrid), or a
+// persistent grid of per_cu workgroups per compute unit that loops over them.
+inline unsigned launch_grid(uint64_t nvb, int per_cu) {
+    uint64_t g = nvb;
+    if (per_cu > 0 && (uint64_t)per_cu * (uint64_t)cu_count() < g)
+        g = (uint64_t)per_cu * (uint64_t)cu_count();
+    return (unsigned)(g < kMaxGrid ? g : kMaxGrid);
 }
 
 // Launch shapes (elements per lane, tiles per lane, sources in flight).
@@ -1043,41 +1096,44 @@ constexpr int epl_for() {
 
 template <int BLOCK, int EPL, int PF>
 void launch_reduce_fl(const uint8_t* ic, const float* is, int32_t K, int64_t c, void* ov,
-                      int32_t odt, float divisor, float rdiv, bool div_fast, hipStream_t st) {
+                      int32_t odt, float divisor, double rdiv, float thr, hipStream_t st) {
     const unsigned nvb = grid_for(c, (int64_t)kThreads * EPL);
     const dim3 grid(launch_grid(nvb, ZPQ_PERSIST_REDUCE));
     if (odt == ZPQ_F32)
         hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EPL, ZPQ_F32, PF>), grid, dim3(kThreads), 0,
-                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, div_fast, nvb);
+                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, thr, nvb);
     else if (odt == ZPQ_F16)
         hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EPL, ZPQ_F16, PF>), grid, dim3(kThreads), 0,
-                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, div_fast, nvb);
+                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, thr, nvb);
     else
         hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EPL, ZPQ_BF16, PF>), grid, dim3(kThreads), 0,
-                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, div_fast, nvb);
+                           st, ic, is, K, c, nullptr, nullptr, ov, divisor, rdiv, thr, nvb);
 }
 
 template <int BLOCK>
 zpq_status launch_reduce(const uint8_t* ic, const float* is, int32_t K, int64_t c, uint8_t* oc,
                          float* os, void* ov, int32_t odt, float divisor, hipStream_t st) {
     constexpr int EI = epl_for<BLOCK, kEplI4>(), EF = epl_for<BLOCK, kEplFl>();
-    const bool div_fast = divisor >= 1.0f && divisor <= 0x1p40f;
-    const float rdiv = 1.0f / divisor;
+    // FLOAT mode: the smallest binary32 thr with thr / divisor >= 2^-126 for
+    // the exact quotient (2^-126 * divisor is exact in binary64; round up).
+    const double rdiv = 1.0 / (double)divisor;
+    const double t64 = ldexp((double)divisor, -126);
+    float thr = (float)t64;
+    if ((double)thr < t64) thr = nextafterf(thr, __builtin_inff());
     if (oc != nullptr) {
         const unsigned nvb = grid_for(c, (int64_t)kThreads * EI);
         hipLaunchKernelGGL((k_dequant_reduce<BLOCK, EI, -1, kPfI4>),
                            dim3(launch_grid(nvb, ZPQ_PERSIST_REDUCE)), dim3(kThreads), 0, st, ic,
-                           is, K, c, oc, os, ov, divisor, rdiv, div_fast, nvb);
+                           is, K, c, oc, os, ov, divisor, rdiv, thr, nvb);
         return after_launch();
     }
     // A short chunk gives few waves at 16 elements per lane (the fused
     // workload's hop 2: 2.6 per SIMD); halving the lane's share doubles them.
     const int64_t waves16 = (c + 16 * 64 - 1) / (16 * 64);
     if (BLOCK <= 256 && waves16 < (int64_t)ZPQ_REDUCE_NARROW_WAVES * 4 * cu_count())
-        launch_reduce_fl<BLOCK, 8, kPfFlNarrow>(ic, is, K, c, ov, odt, divisor, rdiv, div_fast,
-                                                st);
+        launch_reduce_fl<BLOCK, 8, kPfFlNarrow>(ic, is, K, c, ov, odt, divisor, rdiv, thr, st);
     else
-        launch_reduce_fl<BLOCK, EF, kPfFl>(ic, is, K, c, ov, odt, divisor, rdiv, div_fast, st);
+        launch_reduce_fl<BLOCK, EF, kPfFl>(ic, is, K, c, ov, odt, divisor, rdiv, thr, st);
     return after_launch();
 }
 
@@ -1144,18 +1200,20 @@ zpq_status zpq_quant_i8_tensor(const void* x, int32_t x_dtype, int64_t n, int8_t
     }
     hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(kThreads), 0, st, partial, np, scale);
     if (nwg > 0) {
+        const unsigned g = launch_grid((uint64_t)nwg, 0);
+        const uint32_t nvb = (uint32_t)nwg;                 // n <= 2^40: nwg <= 2^28
         switch (x_dtype) {
         case ZPQ_F32:
-            hipLaunchKernelGGL(k_tensor_codes<ZPQ_F32>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
-                               x, n, scale, codes);
+            hipLaunchKernelGGL(k_tensor_codes<ZPQ_F32>, dim3(g), dim3(kThreads), 0, st, x, n,
+                               scale, codes, nvb);
             break;
         case ZPQ_F16:
-            hipLaunchKernelGGL(k_tensor_codes<ZPQ_F16>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
-                               x, n, scale, codes);
+            hipLaunchKernelGGL(k_tensor_codes<ZPQ_F16>, dim3(g), dim3(kThreads), 0, st, x, n,
+                               scale, codes, nvb);
             break;
         default:
-            hipLaunchKernelGGL(k_tensor_codes<ZPQ_BF16>, dim3((unsigned)nwg), dim3(kThreads), 0, st,
-                               x, n, scale, codes);
+            hipLaunchKernelGGL(k_tensor_codes<ZPQ_BF16>, dim3(g), dim3(kThreads), 0, st, x, n,
+                               scale, codes, nvb);
             break;
         }
     }

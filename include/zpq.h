@@ -16,7 +16,12 @@
  *   d = fl32(q * s), rounded to nearest even into the output type.  INT4
  *   codes are two's-complement nibbles, two per byte, element 2k in the low
  *   nibble of byte k.  Results are bit-identical to that definition for all
- *   finite inputs; non-finite inputs give unspecified (but in-bounds) results.
+ *   finite inputs, with two qualifications: where the definition itself
+ *   produces a NaN (a reduced sum that meets +inf and -inf), the result is a
+ *   NaN of unspecified sign and payload; and a block whose reduced sums are
+ *   not all finite has unspecified INT4 codes and scale (the quantizer is
+ *   defined on finite values only).  Non-finite inputs give unspecified (but
+ *   in-bounds) results.
  *
  * Conventions shared by every entry point:
  *   - All buffer arguments are DEVICE pointers owned by the caller; the

@@ -85,3 +85,22 @@ def assert_bits_equal(got, want, what):
     bad = np.nonzero(g != w)[0]
     assert bad.size == 0, (f"{what}: {bad.size} of {g.size} differ; first at {bad[:8].tolist()}: "
                            f"got {g[bad[:8]].tolist()} want {w[bad[:8]].tolist()}")
+
+
+def nan_mask(a, dtype):
+    """Positions holding a NaN, for fp32 / fp16 arrays or bf16 bit patterns."""
+    if dtype == "bf16":
+        b = np.ascontiguousarray(a).view(np.uint16)
+        return ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+    return np.isnan(a)
+
+
+def assert_equal_nan_aware(got, want, dtype, what):
+    """Bit equality, except that where the expected value is a NaN the result
+    must be a NaN of any sign and payload (the definition fixes neither)."""
+    wn = nan_mask(want, dtype)
+    gn = nan_mask(got, dtype)
+    assert np.array_equal(gn, wn), (f"{what}: NaN positions differ: "
+                                    f"{np.nonzero(gn != wn)[0][:8].tolist()}")
+    keep = ~wn
+    assert_bits_equal(np.ascontiguousarray(got)[keep], np.ascontiguousarray(want)[keep], what)

@@ -4,9 +4,8 @@ bf16 absmax a, the scale fl32(a/qmax) from a product and one residual
 correction (a >= 2^-90) equals the IEEE quotient; and for every a with
 s = fl32(a/qmax) >= 2^-100, every value 0 <= x <= a of the same type and
 either float next to the exact 1/s, one residual correction of x * r rounds
-to the same integer as the IEEE quotient fl32(x/s).  (fp32 inputs use two
-corrections with the correctly rounded reciprocal, which Markstein's theorem
-makes exact without enumeration.)"""
+to the same integer as the IEEE quotient fl32(x/s).  (fp32 values take a
+binary64 route instead, checked by tests/test_div_f64.py.)"""
 import os
 import subprocess
 

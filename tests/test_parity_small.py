@@ -6,7 +6,8 @@ import pytest
 
 import block_quantized_communication_amd as zpq
 import oracle
-from parity_util import (adversarial_f32, as_dtype, assert_bits_equal, from_device, to_device)
+from parity_util import (adversarial_f32, as_dtype, assert_bits_equal,
+                         assert_equal_nan_aware, from_device, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,6 +143,43 @@ def test_dequant_reduce_average(out, block, K, divisor):
                                                out_dtype=torch_dt(out), divisor=divisor)
         ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, out, divisor)
         assert_bits_equal(from_device(y), ref, "values")
+
+
+@pytest.mark.parametrize("out", DTYPES)
+@pytest.mark.parametrize("divisor", [1.0, 384.0, 0.5])
+def test_dequant_reduce_average_overflowing_sums(out, divisor):
+    """Sums that overflow, together with a source whose 8*s overflows fp32.
+    Sources 0 and 1 have scales 4e37 (7 * s is finite, two such terms sum past
+    FLT_MAX), source 2 has 4.3e37 (> FLT_MAX/8; -8 * s = -inf already in the
+    definition).  Per element the definition gives +inf, -inf, NaN
+    (+inf + -inf) or a finite value; the average must equal the oracle's,
+    NaN where the oracle has NaN."""
+    rng = np.random.default_rng(404)
+    K, block = 3, 64
+    chunk = (256 * 16 // block * 2 + 3) * block
+    nb = chunk // block
+    codes = rng.integers(0, 256, K * chunk // 2).astype(np.uint8)
+    c = codes.reshape(K, chunk // 2)
+    c[0:2, : chunk // 4] = 0x77          # code 7 in both nibbles: 2 * 7 * 4e37 overflows
+    c[2, : chunk // 8] = 0x88            # code -8 with s > FLT_MAX/8: -inf term
+    s = np.empty((K, nb), np.float32)
+    s[0:2] = np.float32(4e37)
+    s[2] = np.float32(4.3e37)
+    s[:, nb - 5:] = rng.uniform(1e-3, 1.0, (K, 5)).astype(np.float32)   # ordinary tail blocks
+    s = s.ravel()
+    print(f"dequant_reduce_average overflowing sums out={out} divisor={divisor}", flush=True)
+    y = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk, block,
+                                           out_dtype=torch_dt(out), divisor=divisor)
+    ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, out, divisor)
+    got = from_device(y)
+    if out == "bf16":
+        inf_pos = (ref == 0x7F80).sum()
+        nan_pos = (((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)).sum()
+    else:
+        inf_pos = np.isposinf(ref).sum()
+        nan_pos = np.isnan(ref).sum()
+    assert inf_pos > 0 and nan_pos > 0, (inf_pos, nan_pos)   # the case is really exercised
+    assert_equal_nan_aware(got, ref, out, "values")
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
