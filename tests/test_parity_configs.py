@@ -1,27 +1,29 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times.
+benchmark times: every output byte of every kernel is compared with the
+oracle.
 
-Where the oracle is fast enough the whole output is compared (qwZ round
-trip, the qwZ shard, qgZ hop 2).  Elsewhere sampled blocks are compared: the
-oracle recomputes each sampled output block from the generator's input
-through every preceding step (slice reorder, INT4 quantization, hop-1
-reduction), so no oracle input ever comes from the GPU.  Simulated
-all-to-alls: the hop-1 receive buffer of rank (node 0, local 0) is stood in by
-that rank's own L send chunks, and the hop-2 receive buffer by the N send
-positions of its own hop-1 result (same shapes and statistics as the chunks
-other ranks would send).
+The oracle recomputes each output from the generator's input through every
+preceding step (slice reorder, INT4 quantization, hop-1 reduction), so no
+oracle input ever comes from the GPU.  It runs over independent ranges on
+host threads (tests/oracle_ranges.py): whole send positions for the reorder
+and quantization, block ranges of the received chunks for the hop kernels.
+Simulated all-to-alls: the hop-1 receive buffer of rank (node 0, local 0) is
+stood in by that rank's own L send chunks, and the hop-2 receive buffer by
+the N send positions of its own hop-1 result (same shapes and statistics as
+the chunks other ranks would send).
 """
+import time
+
 import numpy as np
 import pytest
 
 import block_quantized_communication_amd as zpq
 import oracle
 import synth
+from oracle_ranges import pmap, source_ranges
 from parity_util import assert_bits_equal, from_device
 
 pytestmark = pytest.mark.gpu
-
-NSAMPLE = 48
 
 
 def torch():
@@ -36,22 +38,44 @@ def dev(a, bf16=False):
     return t.cuda()
 
 
-def gather_bytes(t, starts, width):
-    """Bytes [s, s + width) of a flat CUDA uint8/int8 tensor for each start."""
-    T = torch()
-    idx = (T.as_tensor(np.asarray(starts, np.int64))[:, None] + T.arange(width)[None, :]).cuda()
-    return t.view(T.uint8)[idx.ravel()].cpu().numpy()
+def say(msg):
+    import resource
+    rss = resource.getrusage(resource.RUSAGE_SELF).ru_maxrss / 2 ** 20
+    print(f"[{time.strftime('%H:%M:%S')} peak RSS {rss:.1f} GiB] {msg}", flush=True)
 
 
-def gather_f32(t, idx):
-    T = torch()
-    return t[T.as_tensor(np.asarray(idx, np.int64)).cuda()].cpu().numpy()
+def slice_source(L, N):
+    """Slice carried by each send position, from the oracle's reorder."""
+    return oracle.reorder(np.arange(L * N, dtype=np.int64), L, N)
 
 
-def sample_blocks(rng, nblocks, extra=()):
-    s = set(int(v) for v in rng.integers(0, nblocks, NSAMPLE))
-    s |= {0, nblocks - 1} | {int(v) for v in extra}
-    return np.array(sorted(s), np.int64)
+def oracle_send(g, dtype, L, N, B):
+    """The oracle's reorder + INT4 quantization of the whole gradient, one
+    send position per task: position p carries slice src[p], quantized on
+    its own (its blocks do not depend on any other slice)."""
+    W = L * N
+    S = g.size // W
+    src = slice_source(L, N)
+    parts = pmap(lambda p: oracle.qgz_reorder_quant_i4(g[src[p] * S:(src[p] + 1) * S], dtype,
+                                                       1, 1, B), range(W))
+    return np.concatenate([c for c, _ in parts]), np.concatenate([s for _, s in parts])
+
+
+def oracle_receive(codes, scales, K, chunk, B, ranges, out_dtype=None, divisor=1.0):
+    """The oracle's hop-receive step over K source-major chunks, in `ranges`
+    pieces of the chunk (whole blocks each); returns the concatenation."""
+    R = chunk // ranges
+    assert R * ranges == chunk and R % B == 0
+
+    def one(r):
+        lo, hi = r * R, (r + 1) * R
+        ic = source_ranges(codes, K, chunk // 2, lo // 2, hi // 2)
+        isc = source_ranges(scales, K, chunk // B, lo // B, hi // B)
+        return oracle.qgz_dequant_reduce_requant_i4(ic, isc, K, R, B, out_dtype, divisor)
+    parts = pmap(one, range(ranges))
+    if out_dtype is None:
+        return np.concatenate([c for c, _ in parts]), np.concatenate([s for _, s in parts])
+    return np.concatenate(parts)
 
 
 def test_qwz_roundtrip_full():
@@ -74,14 +98,11 @@ def test_qwz_layer_shard_and_gathered():
     B, W = c["block"], c["world"]
     n = c["n"]
     S = n // W
-    print(f"qwz_layer n={n} shard={S}", flush=True)
+    say(f"qwz_layer n={n} shard={S}: generating")
     layer = synth.qwz_layer()
     xd = dev(layer)
-    # rank 0's shard: full comparison
+    # rank 0's shard
     sc, ss = zpq.quant_i8(xd[:S], B)
-    rc, rs = oracle.quant_i8(layer[:S], "f16", B)
-    assert_bits_equal(from_device(sc), rc, "shard codes")
-    assert_bits_equal(from_device(ss), rs, "shard scales")
     # the gathered buffer: W shards quantized by their ranks and concatenated;
     # shard boundaries are block boundaries, so it is the whole-layer
     # quantization (one launch stands in for the W ranks)
@@ -90,60 +111,43 @@ def test_qwz_layer_shard_and_gathered():
     assert T.equal(gc[:S], sc) and T.equal(gs[:S // B].view(T.int32), ss.view(T.int32))
     y = zpq.dequant_i8(gc, gs, B, T.float16)
     del xd
-    rng = np.random.default_rng(2)
-    nb = n // B
-    blocks = sample_blocks(rng, nb, extra=[r * (S // B) for r in range(W)] +
-                           [r * (S // B) - 1 for r in range(1, W)])
-    xs = np.concatenate([layer[b * B:(b + 1) * B] for b in blocks])
-    ec, es = oracle.quant_i8(xs, "f16", B)
-    ey = oracle.dequant_i8(ec, es, B, "f16")
-    assert_bits_equal(gather_bytes(gc, blocks * B, B).view(np.int8), ec, "gathered codes")
-    assert_bits_equal(gather_f32(gs, blocks), es, "gathered scales")
-    gy = from_device(y)
-    assert_bits_equal(np.concatenate([gy[b * B:(b + 1) * B] for b in blocks]), ey, "dequant")
+    gch, gsh, yh = from_device(gc), from_device(gs), from_device(y)
+    say("qwz_layer: oracle over 48 ranges")
+    R = 1 << 24
+    assert n % R == 0
 
-
-def slice_source(L, N):
-    """Slice carried by each send position, from the oracle's reorder."""
-    return oracle.reorder(np.arange(L * N, dtype=np.int64), L, N)
-
-
-def oracle_send_blocks(g, dtype, L, N, B, positions):
-    """Oracle INT4 codes/scales of the send-order blocks starting at the given
-    positions: each block is gathered from its source slice (the reorder) and
-    quantized on its own (blocks are independent)."""
-    n = g.size
-    S = n // (L * N)
-    src = slice_source(L, N)
-    pos = np.asarray(positions, np.int64)
-    start = src[pos // S] * S + pos % S
-    xs = np.concatenate([g[s:s + B] for s in start])
-    return oracle.qgz_reorder_quant_i4(xs, dtype, 1, 1, B)      # L = N = 1: no reorder
+    def one(r0):
+        ec, es = oracle.quant_i8(layer[r0:r0 + R], "f16", B)
+        return ec, es, oracle.dequant_i8(ec, es, B, "f16")
+    parts = pmap(one, range(0, n, R))
+    ec = np.concatenate([p[0] for p in parts])
+    es = np.concatenate([p[1] for p in parts])
+    assert_bits_equal(gch, ec, "gathered codes")
+    assert_bits_equal(gsh, es, "gathered scales")
+    assert_bits_equal(yh, np.concatenate([p[2] for p in parts]), "dequant")
+    assert_bits_equal(from_device(sc), ec[:S], "shard codes")
+    assert_bits_equal(from_device(ss), es[:S // B], "shard scales")
+    say("qwz_layer: every byte equal")
 
 
 def test_qgz_hop1():
     c = synth.QGZ_HOP1
     L, N, B, n = c["L"], c["N"], c["block"], c["n"]
     chunk = n // L
-    print(f"qgz_hop1 n={n} L={L} N={N} B={B}", flush=True)
+    say(f"qgz_hop1 n={n} L={L} N={N} B={B}: generating")
     g = synth.qgz_hop1()
     c1, s1 = zpq.qgz_reorder_quant_i4(dev(g, bf16=True), L, N, B)
     c2, s2 = zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B)
-    rng = np.random.default_rng(3)
-    S = n // (L * N)
-    # K3, sampled send blocks (including every slice's first and last block)
-    blocks = sample_blocks(rng, n // B, extra=[p * S // B for p in range(L * N)] +
-                           [(p + 1) * S // B - 1 for p in range(L * N)])
-    ec, es = oracle_send_blocks(g, "bf16", L, N, B, blocks * B)
-    assert_bits_equal(gather_bytes(c1, blocks * B // 2, B // 2), ec, "send codes")
-    assert_bits_equal(gather_f32(s1, blocks), es, "send scales")
-    # K4 hop 1, sampled output blocks: source i is send chunk i
-    ob = sample_blocks(rng, chunk // B)
-    pos = np.array([i * chunk + b * B for i in range(L) for b in ob], np.int64)
-    ic, isc = oracle_send_blocks(g, "bf16", L, N, B, pos)         # [i][t] order
-    rc, rs = oracle.qgz_dequant_reduce_requant_i4(ic, isc, L, ob.size * B, B)
-    assert_bits_equal(gather_bytes(c2, ob * B // 2, B // 2), rc, "hop-1 codes")
-    assert_bits_equal(gather_f32(s2, ob), rs, "hop-1 scales")
+    c1h, s1h, c2h, s2h = (from_device(t) for t in (c1, s1, c2, s2))
+    say("qgz_hop1: oracle send buffer")
+    ec1, es1 = oracle_send(g, "bf16", L, N, B)
+    assert_bits_equal(c1h, ec1, "send codes")
+    assert_bits_equal(s1h, es1, "send scales")
+    say("qgz_hop1: oracle hop-1 receive (source i = send chunk i)")
+    ec2, es2 = oracle_receive(ec1, es1, L, chunk, B, 64)
+    assert_bits_equal(c2h, ec2, "hop-1 codes")
+    assert_bits_equal(s2h, es2, "hop-1 scales")
+    say("qgz_hop1: every byte equal")
 
 
 def test_qgz_hop2_full():
@@ -169,40 +173,27 @@ def test_qgz_fused_both_hops():
     W = L * N
     S = n // W
     chunk = n // L
-    print(f"qgz_fused n={n} L={L} N={N} B={B}: generating", flush=True)
+    say(f"qgz_fused n={n} L={L} N={N} B={B}: generating")
     g = synth.qgz_fused()
-    print("qgz_fused: running the three kernels", flush=True)
+    say("qgz_fused: running the three kernels")
     gd = dev(g)
     c1, s1 = zpq.qgz_reorder_quant_i4(gd, L, N, B)
     del gd
     c2, s2 = zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B)
     y = zpq.qgz_dequant_reduce_requant_i4(c2, s2, N, S, B, out_dtype=torch().float16,
                                            divisor=float(W))
-    torch().cuda.synchronize()
-    print("qgz_fused: sampled oracle chain", flush=True)
-    rng = np.random.default_rng(5)
-    ob = sample_blocks(rng, S // B)
-    T = ob.size
-    # level 1: send blocks at i*chunk + m*S + b*B, ordered [m][i][t]
-    pos = np.array([i * chunk + m * S + b * B for m in range(N) for i in range(L) for b in ob],
-                   np.int64)
-    ec1, es1 = oracle_send_blocks(g, "f16", L, N, B, pos)
-    assert_bits_equal(gather_bytes(c1, pos // 2, B // 2), ec1, "send codes")
-    assert_bits_equal(gather_f32(s1, pos // B), es1, "send scales")
-    # level 2: per node position m, reduce the L sources over the T blocks
-    cb, sb = (B // 2) * T, T
-    ec2, es2 = [], []
-    for m in range(N):
-        ic = ec1[m * L * cb:(m + 1) * L * cb]
-        isc = es1[m * L * sb:(m + 1) * L * sb]
-        rc, rs = oracle.qgz_dequant_reduce_requant_i4(ic, isc, L, T * B, B)
-        ec2.append(rc)
-        es2.append(rs)
-    pos2 = np.array([m * S + b * B for m in range(N) for b in ob], np.int64)
-    assert_bits_equal(gather_bytes(c2, pos2 // 2, B // 2), np.concatenate(ec2), "hop-1 codes")
-    assert_bits_equal(gather_f32(s2, pos2 // B), np.concatenate(es2), "hop-1 scales")
-    # level 3: average over the N hop-2 sources
-    ey = oracle.qgz_dequant_reduce_requant_i4(np.concatenate(ec2), np.concatenate(es2), N,
-                                              T * B, B, "f16", float(W))
-    gy = from_device(y)
-    assert_bits_equal(np.concatenate([gy[b * B:(b + 1) * B] for b in ob]), ey, "averaged")
+    c1h, s1h, c2h, s2h, yh = (from_device(t) for t in (c1, s1, c2, s2, y))
+    del c1, s1, c2, s2, y
+    say("qgz_fused: oracle send buffer (384 positions)")
+    ec1, es1 = oracle_send(g, "f16", L, N, B)
+    del g
+    assert_bits_equal(c1h, ec1, "send codes")
+    assert_bits_equal(s1h, es1, "send scales")
+    say("qgz_fused: oracle hop-1 receive")
+    ec2, es2 = oracle_receive(ec1, es1, L, chunk, B, 48)
+    assert_bits_equal(c2h, ec2, "hop-1 codes")
+    assert_bits_equal(s2h, es2, "hop-1 scales")
+    say("qgz_fused: oracle hop-2 receive and average")
+    ey = oracle_receive(ec2, es2, N, S, B, 16, "f16", float(W))
+    assert_bits_equal(yh, ey, "averaged")
+    say("qgz_fused: every byte equal")
