@@ -42,8 +42,10 @@ def parse():
                          "sustained HBM load the chip's power controller lowers the clocks and "
                          "takes tens of ms to settle, and the timed steps should see the settled "
                          "state")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="per-kernel HIP events on every E-th timed step (1: every step)")
+    ap.add_argument("--kernel-samples", type=int, default=20,
+                    help="after the timed steps, run this many more steps with a HIP event pair "
+                         "around every kernel (on the launch stream); per-kernel times are the "
+                         "medians of these samples, whatever --steps is")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.6)
@@ -177,23 +179,31 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Per-kernel HIP event pairs (on the launch stream) on every E-th timed
-    # step: each pair costs the command processor a few microseconds, ten
-    # per step would add ~3% to the step itself.
-    E = max(1, args.event_every)
-    sampled = list(range(0, args.steps, E))
-    ev = {s: [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-              for _ in kernels] for s in sampled}
+    # The timed steps carry no events (an event pair costs the command
+    # processor a few microseconds; around every kernel of every step it
+    # would add ~3% to the step).
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.steps):
-        step(ev.get(s))
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
-    samples_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in sampled]
+
+    # Per-kernel times: a separate pass of --kernel-samples steps with a HIP
+    # event pair around every kernel, on the stream the kernels run on; the
+    # median of the samples.  Each kernel keeps its place in the step (it
+    # reads what the previous kernel did not write), so the last-level cache
+    # holds none of its input.
+    E = max(1, args.kernel_samples)
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in kernels] for _ in range(E)]
+    for s in range(E):
+        step(ev[s])
+    torch.cuda.synchronize()
+    samples_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(E)]
                   for i in range(len(kernels))]
-    per_kernel_ms = [float(np.mean(v)) for v in samples_ms]
+    per_kernel_ms = [float(np.median(v)) for v in samples_ms]
 
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -219,7 +229,7 @@ def main():
     for (name, _, nbytes), ms, smp in zip(kernels, per_kernel_ms, samples_ms):
         gbs = nbytes / (ms * 1e-3) / 1e9
         rows.append({"kernel": name, "bytes": nbytes, "us": round(ms * 1e3, 2),
-                     "us_median": round(float(np.median(smp)) * 1e3, 2),
+                     "us_mean": round(float(np.mean(smp)) * 1e3, 2),
                      "us_min": round(float(np.min(smp)) * 1e3, 2),
                      "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
     dom = max(range(len(rows)), key=lambda i: per_kernel_ms[i])
@@ -247,13 +257,15 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_steps": settle_steps,
-        "kernel_events": f"HIP event pairs around each kernel on {len(sampled)} of the {args.steps} "
-                         f"timed steps (every {E}th), on the launch stream",
+        "kernel_times": f"median of {E} HIP event pairs per kernel on the launch stream, in a "
+                        f"pass of {E} steps after the timed ones",
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "element_types": "fp16 weights and gradients in; INT8 (qwZ) and packed INT4 (qgZ) "
+                         "codes with fp32 scales; fp32 sums; fp16 averaged gradient out",
         "data": "synthetic",
         "config": {
             "workload": "one rank's ZeRO++ quantized-communication step: qwZ on a GPT layer at "
@@ -271,53 +283,71 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def verify(zpq, synth, np, torch, layer_h, grad_h, gath_codes, gath_scales, y_layer, shard_codes,
-           shard_scales, send1_c, send1_s, send2_c, send2_s, y_grad):
-    """Sampled bit-exact check of this run's outputs against the oracle chain
-    computed from the generator's inputs (the parity tests do the same at
-    more samples)."""
+def verify(zpq, synth, np, torch, layer_h, grad_h, gath_codes, gath_scales, y_layer,
+           shard_codes, shard_scales, send1_c, send1_s, send2_c, send2_s, y_grad):
+    """Every output byte of this run against the oracle chain computed from the
+    generator's inputs (never from a GPU output).  The oracle runs over
+    independent ranges on host threads: ranges of the layer for qwZ; send
+    positions, then block ranges of the received chunks, for qgZ."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
-    rng = np.random.default_rng(1234)
+    t0 = time.time()
+    workers = max(1, min(16, os.cpu_count() or 1))
+    pool = ThreadPoolExecutor(workers)
+    host = lambda t: t.view(torch.int16 if t.dtype == torch.float16 else t.dtype).cpu().numpy()
+    same = lambda a, b: bool(np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                                            np.ascontiguousarray(b).view(np.uint8)))
+    ok = {}
     qw, qg = synth.QWZ_LAYER, synth.QGZ_FUSED
-    Bw, Sw = qw["block"], qw["n"] // qw["world"]
-    bl = np.unique(np.concatenate([[0], rng.integers(0, qw["n"] // Bw, 16)]))
-    xs = np.concatenate([layer_h[b * Bw:(b + 1) * Bw] for b in bl])
-    ec, es = oracle.quant_i8(xs, "f16", Bw)
-    ey = oracle.dequant_i8(ec, es, Bw, "f16")
-    gc = gath_codes.cpu().numpy()
-    gy = y_layer.view(torch.int16).cpu().numpy().view(np.uint16)
-    ok = np.array_equal(np.concatenate([gc[b * Bw:(b + 1) * Bw] for b in bl]), ec)
-    ok &= np.array_equal(np.concatenate([gy[b * Bw:(b + 1) * Bw] for b in bl]), ey.view(np.uint16))
-    sb = bl[bl < Sw // Bw]
-    sc = shard_codes.cpu().numpy()
-    ok &= np.array_equal(np.concatenate([sc[b * Bw:(b + 1) * Bw] for b in sb]),
-                         np.concatenate([ec[i * Bw:(i + 1) * Bw] for i, b in enumerate(bl)
-                                         if b < Sw // Bw]))
-    # qgZ: a few final blocks through the whole chain
+    Bw, nw = qw["block"], qw["n"]
+    Sw = nw // qw["world"]
+    R = 1 << 24
+
+    def qwz(r0):
+        c, s = oracle.quant_i8(layer_h[r0:r0 + R], "f16", Bw)
+        return c, s, oracle.dequant_i8(c, s, Bw, "f16")
+    parts = list(pool.map(qwz, range(0, nw, R)))
+    ec = np.concatenate([p[0] for p in parts])
+    es = np.concatenate([p[1] for p in parts])
+    ok["qwz_gathered_codes"] = same(host(gath_codes), ec)
+    ok["qwz_gathered_scales"] = same(host(gath_scales), es)
+    ok["qwz_dequant"] = same(host(y_layer), np.concatenate([p[2] for p in parts]))
+    ok["qwz_shard_codes"] = same(host(shard_codes), ec[:Sw])
+    ok["qwz_shard_scales"] = same(host(shard_scales), es[:Sw // Bw])
+    del parts, ec, es
+
     L, N, B, n = qg["L"], qg["N"], qg["block"], qg["n"]
-    S, chunk = n // (L * N), n // L
-    ob = np.unique(rng.integers(0, S // B, 4))
-    src = oracle.reorder(np.arange(L * N, dtype=np.int64), L, N)
-    pos = np.array([i * chunk + m * S + b * B for m in range(N) for i in range(L) for b in ob])
-    start = src[pos // S] * S + pos % S
-    c1, s1 = oracle.qgz_reorder_quant_i4(np.concatenate([grad_h[s:s + B] for s in start]), "f16",
-                                         1, 1, B)
-    T = ob.size
-    cb = (B // 2) * T
-    c2 = []
-    s2 = []
-    for m in range(N):
-        rc, rs = oracle.qgz_dequant_reduce_requant_i4(c1[m * L * cb:(m + 1) * L * cb],
-                                                      s1[m * L * T:(m + 1) * L * T], L, T * B, B)
-        c2.append(rc)
-        s2.append(rs)
-    ey = oracle.qgz_dequant_reduce_requant_i4(np.concatenate(c2), np.concatenate(s2), N, T * B, B,
-                                              "f16", float(L * N))
-    yg = y_grad.view(torch.int16).cpu().numpy().view(np.uint16)
-    ok &= np.array_equal(np.concatenate([yg[b * B:(b + 1) * B] for b in ob]), ey.view(np.uint16))
-    s1g = send1_c.cpu().numpy()
-    ok &= np.array_equal(np.concatenate([s1g[p // 2:p // 2 + B // 2] for p in pos]), c1)
-    return {"sampled_blocks": int(bl.size + pos.size + ob.size), "bit_exact": bool(ok)}
+    W = L * N
+    S, chunk = n // W, n // L
+    src = oracle.reorder(np.arange(W, dtype=np.int64), L, N)
+    parts = list(pool.map(lambda p: oracle.qgz_reorder_quant_i4(
+        grad_h[src[p] * S:(src[p] + 1) * S], "f16", 1, 1, B), range(W)))
+    c1 = np.concatenate([p[0] for p in parts])
+    s1 = np.concatenate([p[1] for p in parts])
+    ok["qgz_send_codes"] = same(host(send1_c), c1)
+    ok["qgz_send_scales"] = same(host(send1_s), s1)
+
+    def receive(codes, scales, K, ch, pieces, out_dtype=None, divisor=1.0):
+        r = ch // pieces
+
+        def one(k):
+            lo, hi = k * r, (k + 1) * r
+            ic = np.concatenate([codes[i * (ch // 2) + lo // 2:i * (ch // 2) + hi // 2]
+                                 for i in range(K)])
+            isc = np.concatenate([scales[i * (ch // B) + lo // B:i * (ch // B) + hi // B]
+                                  for i in range(K)])
+            return oracle.qgz_dequant_reduce_requant_i4(ic, isc, K, r, B, out_dtype, divisor)
+        return list(pool.map(one, range(pieces)))
+    parts = receive(c1, s1, L, chunk, 48)         # hop-1 receive: this rank's own send chunks
+    c2 = np.concatenate([p[0] for p in parts])
+    s2 = np.concatenate([p[1] for p in parts])
+    ok["qgz_hop1_codes"] = same(host(send2_c), c2)
+    ok["qgz_hop1_scales"] = same(host(send2_s), s2)
+    y = np.concatenate(receive(c2, s2, N, S, 16, "f16", float(W)))
+    ok["qgz_hop2_average"] = same(host(y_grad), y)
+    pool.shutdown()
+    return {"compared": "every output byte of every kernel of this run", "bit_exact": all(ok.values()),
+            "parts": ok, "oracle_threads": workers, "seconds": round(time.time() - t0, 1)}
 
 
 def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):
@@ -549,6 +579,25 @@ def blocking_study(np, torch, zpq, synth, reps=20):
             "error": "RMS(dequant(quant(x)) - x) / RMS(x) in fp64; max |error|"}
 
 
+def host_cpu():
+    """CPU model and core counts of the host the oracle ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": usable, "os_cpu_count": os.cpu_count(),
+            "threads_used": 1}
+
+
 def cpu_baseline(np, layer_h, grad_h, frac):
     """The oracle (plain single-threaded C) on a fraction of every kernel's
     step work, same block sizes and the same L, N; GB/s over the same
@@ -587,7 +636,7 @@ def cpu_baseline(np, layer_h, grad_h, frac):
               (L * (c4 // 2 + (c4 // B) * 4) + c4 // 2 + (c4 // B) * 4) +
               (N * (c5 // 2 + (c5 // B) * 4) + c5 * 2))
     return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"{frac:.4g} of every kernel's step work (qwZ shard {n1} and gathered "
                       f"{n2} elements, qgZ gradient {n3} elements, hop-1 chunk {c4}, hop-2 "
                       f"slice {c5}; same blocks, L, N); {secs:.1f} s of single-threaded oracle "

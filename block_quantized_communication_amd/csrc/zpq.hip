@@ -312,8 +312,12 @@ struct BlockScale {
     template <int N>
     __device__ __forceinline__ void codes(const float (&v)[N], uint32_t (&out)[N]) {
         if constexpr (ONE_STEP) {
-            if (!fast) s = a / (float)QMAX;
-            codes16<QMAX>(s, r, fast, v, out);
+            if (fast) {
+                codes16<QMAX>(s, r, true, v, out);
+            } else {
+                s = a / (float)QMAX;
+                codes16<QMAX>(s, r, false, v, out);
+            }
         } else {
             codes32<QMAX>(rd, fast, v, out);
         }
