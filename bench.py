@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--per-config", action="store_true",
                     help="time every kernel at every workload size (cache evicted before each "
                          "launch) instead of the step")
+    ap.add_argument("--patterns", action="store_true",
+                    help="time every kernel at every workload size beside its bare access pattern "
+                         "(the same loads and stores without the arithmetic, from "
+                         "bench_patterns.hip) and the read / write / copy ceilings")
     ap.add_argument("--study", choices=["hop-count", "blocking"], default=None,
                     help="run an error study instead of the throughput benchmark")
     ap.add_argument("--copy-probe", action="store_true",
@@ -87,6 +91,9 @@ def main():
         return
     if args.per_config:
         print(json.dumps(per_config(np, torch, zpq, synth)), flush=True)
+        return
+    if args.patterns:
+        print(json.dumps(patterns(np, torch, zpq, synth)), flush=True)
         return
 
     torch.cuda.set_device(0)
@@ -519,6 +526,172 @@ def per_config(np, torch, zpq, synth, reps=50, settle_s=0.2):
     return {"per_config": rows, "timing": f"median of {reps} single launches, HIP events, "
             "1 GiB read-only pass before each launch, 200 ms settle per kernel",
             "peak_GBps": HBM_PEAK_GBS}
+
+
+def patterns(np, torch, zpq, synth, reps=50, settle_s=0.2):
+    """Each kernel at each workload size beside its bare access pattern, and
+    the streaming ceilings.  The pattern kernels (bench_patterns.hip) issue
+    the same per-lane loads and stores as the kernel -- widths, cache hints,
+    lane layout, tiles per lane, sources in flight, grid, slice reorder --
+    with XOR in place of the arithmetic.  Timing as --per-config: a 1 GiB
+    read-only pass before every launch (the last-level cache holds nothing of
+    the launch's data), HIP events on the launch stream, medians of `reps`
+    launches; kernel and pattern alternate in rounds of 10 so that both see
+    the same clock state."""
+    import ctypes
+    path = os.path.join(ROOT, "libbench_patterns.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libbench_patterns.so is missing: run __graft_entry__.build()")
+    P = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P.pat_read.argtypes = [vp, i64, vp, vp]
+    P.pat_write.argtypes = [vp, i64, vp]
+    P.pat_copy.argtypes = [vp, vp, i64, vp]
+    P.pat_quant_i8.argtypes = [vp, i64, vp, vp, vp]
+    P.pat_dequant_i8.argtypes = [vp, vp, i64, vp, vp]
+    P.pat_reorder_quant_i4.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
+    P.pat_receive.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, vp]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T = torch
+    st = torch.cuda.current_stream()
+    S_ = ctypes.c_void_p(st.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    null = ctypes.c_void_p(0)
+    e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"pattern launch failed ({rc})")
+
+    def time_pair(fns):
+        """Median microseconds of each function, evicting before each launch."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for f in fns:
+                scratch.max()
+                f()
+            torch.cuda.synchronize()
+        us = [[] for _ in fns]
+        for _ in range(reps // 10):
+            for k, f in enumerate(fns):
+                ev = []
+                for _ in range(10):
+                    scratch.max()
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(st)
+                    f()
+                    b.record(st)
+                    ev.append((a, b))
+                torch.cuda.synchronize()
+                us[k] += [a.elapsed_time(b) * 1e3 for a, b in ev]
+        return [float(np.median(u)) for u in us]
+
+    rows = []
+
+    def row(label, nbytes, kfn, pfn):
+        k_us, p_us = time_pair([kfn, pfn])
+        rows.append({"kernel": label, "bytes": int(nbytes), "kernel_us": round(k_us, 2),
+                     "pattern_us": round(p_us, 2),
+                     "kernel_frac_of_peak": round(nbytes / k_us / 1e3 / HBM_PEAK_GBS, 4),
+                     "pattern_frac_of_peak": round(nbytes / p_us / 1e3 / HBM_PEAK_GBS, 4),
+                     "kernel_over_pattern": round(k_us / p_us, 3)})
+        print(f"[patterns] {label}: kernel {k_us:.1f} us, pattern {p_us:.1f} us",
+              file=sys.stderr, flush=True)
+
+    def receive_shape(c, K, fl):
+        if not fl:
+            return 32, 2
+        waves16 = (c + 16 * 64 - 1) // (16 * 64)
+        return (8, 4) if waves16 < 8 * 4 * cus else (16, 2)
+
+    # ceilings: 1 GiB streams
+    nb = 1 << 30
+    a, b = e(nb // 4, T.float32), e(nb // 4, T.float32)
+    a.fill_(1.0)
+    sink = e(256, T.int32)
+    ceil = {}
+    for name, f, moved in (("read", lambda: ok(P.pat_read(ptr(a), nb, ptr(sink), S_)), nb),
+                           ("write", lambda: ok(P.pat_write(ptr(b), nb, S_)), nb),
+                           ("copy", lambda: ok(P.pat_copy(ptr(a), ptr(b), nb, S_)), 2 * nb)):
+        (us,) = time_pair([f])
+        ceil[name] = {"bytes": moved, "us": round(us, 2), "GBps": round(moved / us / 1e3, 1),
+                      "frac_of_peak": round(moved / us / 1e3 / HBM_PEAK_GBS, 4)}
+        print(f"[patterns] {name} ceiling: {moved / us / 1e3:.0f} GB/s", file=sys.stderr, flush=True)
+    del a, b
+
+    # c2: qwZ on the h8192 layer
+    c = synth.QWZ_LAYER
+    n, B, W = c["n"], c["block"], c["world"]
+    S = n // W
+    layer = torch.from_numpy(synth.qwz_layer()).to(dev)
+    sc, ss, pc, ps = e(S, T.int8), e(S // B, T.float32), e(S, T.int8), e(S // B, T.float32)
+    row("c2 K1 quant_i8 shard 50.3M fp16 B=256", S * 3 + S // B * 4,
+        lambda: zpq.quant_i8(layer[:S], B, out=(sc, ss), stream=st),
+        lambda: ok(P.pat_quant_i8(ptr(layer), S, ptr(pc), ptr(ps), S_)))
+    gc, gs, y, py = e(n, T.int8), e(n // B, T.float32), e(n, T.float16), e(n, T.float16)
+    zpq.quant_i8(layer, B, out=(gc, gs), stream=st)
+    del layer, sc, ss, pc, ps
+    row("c2 K2 dequant_i8 gathered 805M -> fp16", n * 3 + n // B * 4,
+        lambda: zpq.dequant_i8(gc, gs, B, out=y, stream=st),
+        lambda: ok(P.pat_dequant_i8(ptr(gc), ptr(gs), n, ptr(py), S_)))
+    del gc, gs, y, py
+
+    def qgz_rows(tag, g, dt_bytes, L, N, B, out_dt, fl2_label, fl1_label, k3_label):
+        n = g.numel()
+        W = L * N
+        S, chunk = n // W, n // L
+        c1, s1, p1, q1 = e(n // 2, T.uint8), e(n // B, T.float32), e(n // 2, T.uint8), e(n // B, T.float32)
+        row(k3_label, n * dt_bytes + n // 2 + n // B * 4,
+            lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1), stream=st),
+            lambda: ok(P.pat_reorder_quant_i4(ptr(g), n, L, N, B, ptr(p1), ptr(q1), S_)))
+        c2, s2, p2, q2 = (e(chunk // 2, T.uint8), e(chunk // B, T.float32), e(chunk // 2, T.uint8),
+                          e(chunk // B, T.float32))
+        epl, pf = receive_shape(chunk, L, False)
+        row(fl1_label, L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4,
+            lambda: zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B, out=(c2, s2), stream=st),
+            lambda: ok(P.pat_receive(ptr(c1), ptr(s1), L, chunk, B, ptr(p2), ptr(q2), null, epl, pf,
+                                     S_)))
+        if fl2_label:
+            yv, pv = e(S, out_dt), e(S, out_dt)
+            epl, pf = receive_shape(S, N, True)
+            row(fl2_label, N * (S // 2 + S // B * 4) + S * 2,
+                lambda: zpq.qgz_dequant_reduce_requant_i4(c2, s2, N, S, B, out_dtype=out_dt,
+                                                          divisor=float(W), out=yv, stream=st),
+                lambda: ok(P.pat_receive(ptr(c2), ptr(s2), N, S, B, null, null, ptr(pv), epl, pf,
+                                         S_)))
+
+    # c3: qgZ hop 1
+    c = synth.QGZ_HOP1
+    g = torch.from_numpy(synth.qgz_hop1()).view(T.bfloat16).to(dev)
+    qgz_rows("c3", g, 2, c["L"], c["N"], c["block"], None, None,
+             "c3 K4 hop-1 8 x 2^25 -> INT4", "c3 K3 reorder_quant_i4 2^28 bf16 L=8 N=4 B=128")
+    del g
+    # c4: qgZ hop 2, 16 x 2^24 -> bf16
+    c = synth.QGZ_HOP2
+    K, chunk, B = c["sources"], c["chunk"], c["block"]
+    src = torch.from_numpy(np.concatenate([synth.qgz_hop2_source(i) for i in range(K)])).to(dev)
+    ic, isc = zpq.qgz_reorder_quant_i4(src, 1, 1, B)
+    del src
+    yv, pv = e(chunk, T.bfloat16), e(chunk, T.bfloat16)
+    epl, pf = receive_shape(chunk, K, True)
+    row("c4 K5 hop-2 16 x 2^24 -> bf16 average", K * (chunk // 2 + chunk // B * 4) + chunk * 2,
+        lambda: zpq.qgz_dequant_reduce_requant_i4(ic, isc, K, chunk, B, out_dtype=T.bfloat16,
+                                                  divisor=c["divisor"], out=yv, stream=st),
+        lambda: ok(P.pat_receive(ptr(ic), ptr(isc), K, chunk, B, null, null, ptr(pv), epl, pf, S_)))
+    del ic, isc, yv, pv
+    # c5: fused qgZ
+    c = synth.QGZ_FUSED
+    g = torch.from_numpy(synth.qgz_fused()).to(dev)
+    qgz_rows("c5", g, 2, c["L"], c["N"], c["block"], T.float16,
+             "c5 K5 hop-2 48 x 2.75M -> fp16 average", "c5 K4 hop-1 8 x 132M -> INT4",
+             "c5 K3 reorder_quant_i4 1.06G fp16 L=8 N=48 B=64")
+    return {"patterns": rows, "ceilings_1GiB": ceil,
+            "timing": f"median of {reps} single launches per kernel and per pattern, HIP events, "
+                      "1 GiB read-only pass before each launch, kernel and pattern alternating in "
+                      "rounds of 10", "peak_GBps": HBM_PEAK_GBS}
 
 
 def blocking_study(np, torch, zpq, synth, reps=20):

@@ -1,0 +1,317 @@
+// bench_patterns.hip -- measurement kernels for bench.py --patterns (not part
+// of libzpq; built into libbench_patterns.so beside bench.py).
+//
+// Two kinds:
+//  * ceilings: read-only, write-only and copy streams, 16 bytes per lane and
+//    tile, non-temporal, two tiles per lane, one-shot grids of 256-thread
+//    workgroups -- what plain streaming reaches on this GPU;
+//  * access patterns: for each libzpq kernel, the same per-lane loads and
+//    stores (widths, cache hints, lane layout, tiles per lane, sources in
+//    flight, grid shape, the slice reorder of the qgZ quantizer) with the
+//    arithmetic replaced by XOR -- what the kernel's memory traffic alone
+//    costs.  Their outputs are meaningless.
+//
+// Every entry point takes device pointers and a hipStream_t, checks nothing
+// beyond what its caller (bench.py) guarantees (whole tiles / blocks, the
+// sizes of the workloads), and returns the hipGetLastError code.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T>
+__device__ __forceinline__ T ldnt(const T* p) { return __builtin_nontemporal_load(p); }
+template <class T>
+__device__ __forceinline__ void stnt(T v, T* p) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+// ---------------------------------------------------------------------------
+// Ceilings.  n16 = number of 16-byte units; tile = 256 lanes x 16 bytes.
+__global__ __launch_bounds__(kThreads) void k_read(const u32x4* __restrict__ src, int64_t n16,
+                                                   uint32_t* __restrict__ sink) {
+    const int64_t base = (int64_t)blockIdx.x * (2 * kThreads);
+    uint32_t x = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t i = base + u * kThreads + threadIdx.x;
+        if (i < n16) x ^= fold(ldnt(src + i));
+    }
+    if (x == 0x9E3779B9u) sink[threadIdx.x] = x;      // keeps the loads; practically never taken
+}
+
+__global__ __launch_bounds__(kThreads) void k_write(u32x4* __restrict__ dst, int64_t n16) {
+    const int64_t base = (int64_t)blockIdx.x * (2 * kThreads);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t i = base + u * kThreads + threadIdx.x;
+        if (i < n16) stnt(u32x4{(uint32_t)i, 1u, 2u, 3u}, dst + i);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, int64_t n16) {
+    const int64_t base = (int64_t)blockIdx.x * (2 * kThreads);
+    u32x4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t i = base + u * kThreads + threadIdx.x;
+        v[u] = i < n16 ? ldnt(src + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t i = base + u * kThreads + threadIdx.x;
+        if (i < n16) stnt(v[u], dst + i);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// qwZ quantize (fp16 in, block 256): per lane and tile one 16-byte load (8
+// elements), one 8-byte code store, one scale store per 32 lanes; two tiles
+// per lane.
+__global__ __launch_bounds__(kThreads) void k_pat_quant_i8(const u32x4* __restrict__ x, int64_t n,
+                                                           u32x2* __restrict__ codes,
+                                                           uint32_t* __restrict__ scales) {
+    const int64_t base = (int64_t)blockIdx.x * (2 * kThreads * 8);
+    u32x4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t e = base + u * (kThreads * 8) + threadIdx.x * 8;
+        v[u] = e < n ? ldnt(x + e / 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t e = base + u * (kThreads * 8) + threadIdx.x * 8;
+        if (e < n) {
+            stnt(u32x2{v[u].x ^ v[u].y, v[u].z ^ v[u].w}, codes + e / 8);
+            if ((threadIdx.x & 31) == 0) scales[e / 256] = fold(v[u]);
+        }
+    }
+}
+
+// qwZ dequantize (block 256, fp16 out): per lane one 8-byte code load, one
+// scale load, one 16-byte store; workgroups in the XCD-contiguous tile order.
+__global__ __launch_bounds__(kThreads) void k_pat_dequant_i8(const u32x2* __restrict__ codes,
+                                                             const uint32_t* __restrict__ scales,
+                                                             int64_t n, u32x4* __restrict__ y,
+                                                             uint32_t nvb) {
+    const uint32_t k = blockIdx.x, xcd = k & 7u, i = k >> 3, q = nvb >> 3, r = nvb & 7u;
+    const uint32_t vb = xcd * q + (xcd < r ? xcd : r) + i;
+    const int64_t e = (int64_t)vb * (kThreads * 8) + threadIdx.x * 8;
+    if (e < n) {
+        const u32x2 c = ldnt(codes + e / 8);
+        const uint32_t s = scales[e / 256];
+        stnt(u32x4{c.x ^ s, c.y, c.x, c.y ^ s}, y + e / 8);
+    }
+}
+
+// qgZ reorder + INT4 quantize (fp16/bf16 in, block 64 or 128): slice-major
+// workgroups (send position p = j*N + m reads slice m*L + j), two tiles per
+// lane, one 16-byte load and one 4-byte code store per lane and tile, one
+// scale store per block.
+__global__ __launch_bounds__(kThreads) void k_pat_reorder_quant_i4(
+    const u32x4* __restrict__ g, int64_t S, int32_t L, int32_t N, uint32_t wgs_per_slice,
+    int32_t block, uint32_t* __restrict__ codes, uint32_t* __restrict__ scales) {
+    const uint32_t vb = blockIdx.x;
+    const uint32_t p = vb / wgs_per_slice, w = vb - p * wgs_per_slice;
+    const uint32_t j = p / (uint32_t)N, m = p - j * (uint32_t)N;
+    const int64_t src0 = ((int64_t)m * L + j) * S, dst0 = (int64_t)p * S;
+    const int64_t f0 = (int64_t)w * (2 * kThreads * 8);
+    const uint32_t lanes_per_block = (uint32_t)block / 8;
+    u32x4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t f = f0 + u * (kThreads * 8) + threadIdx.x * 8;
+        v[u] = f < S ? ldnt(g + (src0 + f) / 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t f = f0 + u * (kThreads * 8) + threadIdx.x * 8;
+        if (f < S) {
+            const int64_t e = dst0 + f;
+            stnt(fold(v[u]), codes + e / 8);
+            if ((threadIdx.x & (lanes_per_block - 1)) == 0) scales[e / block] = v[u].x;
+        }
+    }
+}
+
+// qgZ hop receive: per lane EPL nibbles (EPL/2 bytes) and one scale from each
+// of K sources, PF sources in flight, through buffer descriptors that cover
+// one source each (as the kernel reads them); then EPL/2 bytes of codes and a
+// scale per block (INT4 output) or EPL 16-bit values (float output).
+constexpr int kAux = 2;        // non-temporal loads
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int EPL>
+struct Src {
+    uint32_t w[EPL / 8];
+    uint32_t s;
+};
+
+template <int EPL>
+__device__ __forceinline__ void load(Src<EPL>& d, const uint8_t* c, uint32_t cb, uint32_t coff,
+                                     const uint32_t* s, uint32_t sb, uint32_t soff) {
+    const __amdgpu_buffer_rsrc_t rc = rsrc(c, cb);
+    if constexpr (EPL == 8) {
+        d.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, coff, 0, kAux);
+    } else if constexpr (EPL == 16) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b64(rc, coff, 0, kAux);
+        d.w[0] = t[0]; d.w[1] = t[1];
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL / 32; ++i) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b128(rc, coff + 16 * i, 0, kAux);
+            d.w[4 * i] = t[0]; d.w[4 * i + 1] = t[1]; d.w[4 * i + 2] = t[2]; d.w[4 * i + 3] = t[3];
+        }
+    }
+    d.s = __builtin_amdgcn_raw_buffer_load_b32(rsrc(s, sb), soff * 4, 0, 0);
+}
+
+template <int EPL>
+__device__ __forceinline__ void mix(uint32_t (&acc)[EPL / 8], const Src<EPL>& d) {
+#pragma unroll
+    for (int i = 0; i < EPL / 8; ++i) acc[i] ^= d.w[i] ^ d.s;
+}
+
+template <int EPL, int PF, bool I4>
+__global__ __launch_bounds__(kThreads) void k_pat_receive(
+    const uint8_t* __restrict__ in_codes, const uint32_t* __restrict__ in_scales, int32_t K,
+    int64_t c, int32_t block, uint8_t* __restrict__ out_codes, uint32_t* __restrict__ out_scales,
+    uint16_t* __restrict__ out_vals) {
+    const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * EPL;
+    if (e >= c) return;
+    const int64_t cs = c / 2, ss = c / block;
+    const uint32_t coff = (uint32_t)(e / 2), soff = (uint32_t)(e / block);
+    const uint32_t cb = (uint32_t)cs, sb = (uint32_t)(ss * 4);
+    uint32_t acc[EPL / 8] = {};
+    auto ld = [&](Src<EPL>& d, int i) {
+        load<EPL>(d, in_codes + (int64_t)i * cs, cb, coff, in_scales + (int64_t)i * ss, sb, soff);
+    };
+    Src<EPL> buf[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) ld(buf[k], k);            // K >= PF (bench.py's workloads)
+    int i0 = 0;
+    for (; i0 + 2 * PF <= K; i0 += PF) {
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            mix<EPL>(acc, buf[k]);
+            ld(buf[k], i0 + PF + k);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < PF; ++k) mix<EPL>(acc, buf[k]);
+    for (int i = i0 + PF; i < K; ++i) {
+        Src<EPL> d;
+        ld(d, i);
+        mix<EPL>(acc, d);
+    }
+    if constexpr (I4) {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(out_codes + e / 2);
+#pragma unroll
+        for (int i = 0; i < EPL / 8; i += 4) {
+            if constexpr (EPL >= 32)
+                stnt(u32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]},
+                     reinterpret_cast<u32x4*>(dst + i));
+        }
+        if constexpr (EPL == 16) stnt(u32x2{acc[0], acc[1]}, reinterpret_cast<u32x2*>(dst));
+        if constexpr (EPL == 8) stnt(acc[0], dst);
+        const uint32_t lanes_per_block = (uint32_t)block / EPL;
+        if ((threadIdx.x & (lanes_per_block - 1)) == 0) out_scales[e / block] = acc[0];
+    } else {
+        u32x4* dst = reinterpret_cast<u32x4*>(out_vals + e);
+#pragma unroll
+        for (int k = 0; k < EPL / 8; ++k) stnt(u32x4{acc[k], acc[k] + 1, acc[k] + 2, acc[k] + 3}, dst + k);
+    }
+}
+
+inline unsigned grid_for(int64_t units, int64_t per_wg) {
+    return (unsigned)((units + per_wg - 1) / per_wg);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pat_read(const void* src, int64_t bytes, void* sink, void* st) {
+    const int64_t n16 = bytes / 16;
+    hipLaunchKernelGGL(k_read, dim3(grid_for(n16, 2 * kThreads)), dim3(kThreads), 0,
+                       (hipStream_t)st, (const u32x4*)src, n16, (uint32_t*)sink);
+    return hipGetLastError();
+}
+
+int pat_write(void* dst, int64_t bytes, void* st) {
+    const int64_t n16 = bytes / 16;
+    hipLaunchKernelGGL(k_write, dim3(grid_for(n16, 2 * kThreads)), dim3(kThreads), 0,
+                       (hipStream_t)st, (u32x4*)dst, n16);
+    return hipGetLastError();
+}
+
+int pat_copy(const void* src, void* dst, int64_t bytes, void* st) {
+    const int64_t n16 = bytes / 16;
+    hipLaunchKernelGGL(k_copy, dim3(grid_for(n16, 2 * kThreads)), dim3(kThreads), 0,
+                       (hipStream_t)st, (const u32x4*)src, (u32x4*)dst, n16);
+    return hipGetLastError();
+}
+
+// n fp16 elements, block 256
+int pat_quant_i8(const void* x, int64_t n, void* codes, void* scales, void* st) {
+    hipLaunchKernelGGL(k_pat_quant_i8, dim3(grid_for(n, 2 * kThreads * 8)), dim3(kThreads), 0,
+                       (hipStream_t)st, (const u32x4*)x, n, (u32x2*)codes, (uint32_t*)scales);
+    return hipGetLastError();
+}
+
+// n elements, block 256, fp16 out
+int pat_dequant_i8(const void* codes, const void* scales, int64_t n, void* y, void* st) {
+    const unsigned nvb = grid_for(n, kThreads * 8);
+    hipLaunchKernelGGL(k_pat_dequant_i8, dim3(nvb), dim3(kThreads), 0, (hipStream_t)st,
+                       (const u32x2*)codes, (const uint32_t*)scales, n, (u32x4*)y, nvb);
+    return hipGetLastError();
+}
+
+// n fp16/bf16 elements, L x N slices, block 64 or 128
+int pat_reorder_quant_i4(const void* g, int64_t n, int32_t L, int32_t N, int32_t block,
+                         void* codes, void* scales, void* st) {
+    const int64_t S = n / ((int64_t)L * N);
+    const unsigned wps = grid_for(S, 2 * kThreads * 8);
+    hipLaunchKernelGGL(k_pat_reorder_quant_i4, dim3(wps * (unsigned)(L * N)), dim3(kThreads), 0,
+                       (hipStream_t)st, (const u32x4*)g, S, L, N, wps, block, (uint32_t*)codes,
+                       (uint32_t*)scales);
+    return hipGetLastError();
+}
+
+// K sources x c elements; I4 output (out_codes, out_scales) when out_vals is
+// NULL, else 16-bit values.  epl / pf: the launch shape libzpq picks.
+int pat_receive(const void* in_codes, const void* in_scales, int32_t K, int64_t c, int32_t block,
+                void* out_codes, void* out_scales, void* out_vals, int32_t epl, int32_t pf,
+                void* st) {
+    const unsigned g = grid_for(c, (int64_t)kThreads * epl);
+    const hipStream_t s = (hipStream_t)st;
+    const uint8_t* ic = (const uint8_t*)in_codes;
+    const uint32_t* is = (const uint32_t*)in_scales;
+    uint8_t* oc = (uint8_t*)out_codes;
+    uint32_t* os = (uint32_t*)out_scales;
+    uint16_t* ov = (uint16_t*)out_vals;
+    if (!out_vals && epl == 32 && pf == 2)
+        hipLaunchKernelGGL((k_pat_receive<32, 2, true>), dim3(g), dim3(kThreads), 0, s, ic, is, K,
+                           c, block, oc, os, ov);
+    else if (out_vals && epl == 16 && pf == 2)
+        hipLaunchKernelGGL((k_pat_receive<16, 2, false>), dim3(g), dim3(kThreads), 0, s, ic, is, K,
+                           c, block, oc, os, ov);
+    else if (out_vals && epl == 8 && pf == 4)
+        hipLaunchKernelGGL((k_pat_receive<8, 4, false>), dim3(g), dim3(kThreads), 0, s, ic, is, K,
+                           c, block, oc, os, ov);
+    else
+        return (int)hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // extern "C"
