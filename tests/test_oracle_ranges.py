@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-import test_parity_configs as cfg
+import oracle_ranges as cfg
 
 
 @pytest.mark.parametrize("L,N,B,per", [(2, 3, 64, 4096), (8, 4, 128, 2048), (3, 5, 32, 640)])
