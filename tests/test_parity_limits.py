@@ -104,3 +104,29 @@ def test_dequant_reduce_past_2p31(mode):
         ry = oracle.qgz_dequant_reduce_requant_i4(ic, isc, K, m, B, "bf16", 16.0)
         got = rows(y.view(T.int16), bl, B).numpy().view(np.uint16)
         assert_bits_equal(got, ry, "values")
+
+
+def test_dequant_i8_beyond_one_dispatch_grid():
+    """2^35 + 2^12 elements: 2^24 + 2 workgroup tiles of 2048 elements, more
+    than one dispatch can launch (2^32 - 1 work-items); the grid is capped and
+    the first workgroups take a second tile.  Sampled: the first and last
+    blocks, random blocks and every block of the three tiles that the second
+    pass covers (with the XCD-contiguous tile order, tiles 2^21, 2^22 + 1 and
+    2^24 + 1).  Needs about 97 GB of device memory."""
+    T = torch()
+    B, n = 256, (1 << 35) + (1 << 12)
+    T.cuda.empty_cache()
+    print(f"dequant_i8 n={n}: drawing codes", flush=True)
+    codes = T.randint(-128, 128, (n,), generator=gen(15), device="cuda", dtype=T.int8)
+    scales = T.rand(n // B, generator=gen(16), device="cuda") * 0.01
+    y = zpq.dequant_i8(codes, scales, B, T.float16)
+    T.cuda.synchronize()
+    tiles = [1 << 21, (1 << 22) + 1, (1 << 24) + 1]
+    s = {0, 1, n // B - 1} | {int(v) for v in np.random.default_rng(15).integers(0, n // B, 32)}
+    s |= {t * 8 + k for t in tiles for k in range(-1, 9)}
+    bl = np.array(sorted(b for b in s if 0 <= b < n // B), np.int64)
+    cs = rows(codes, bl, B).numpy()
+    ss = scales[T.as_tensor(bl).cuda()].cpu().numpy()
+    assert_bits_equal(rows(y, bl, B).numpy(), oracle.dequant_i8(cs, ss, B, "f16"), "dequant")
+    del codes, scales, y
+    T.cuda.empty_cache()
