@@ -31,6 +31,52 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective HBM GB/s per kernel and % of MI355X peak (qwZ quant/dequant, qgZ hop)"
 
+# Kernel time, everywhere in this file: the per-launch time of launches issued
+# back to back on one stream (one HIP event pair around `LAUNCHES` launches,
+# median over groups), cycling through enough distinct buffer sets that no
+# launch finds its data in the 256 MB last-level cache.  Back-to-back launches
+# hide the dispatch of each kernel behind the previous one, as in a pipeline:
+# this is the duration the rocprofv3 kernel trace reports, while an event pair
+# around a single launch adds 2-4 us of command-processor time.
+LAUNCHES = 20
+ROTATE_BYTES = 640 << 20          # data touched between two uses of a buffer set
+
+
+def n_sets(bytes_per_launch):
+    """Buffer sets needed so that ROTATE_BYTES pass between two uses of one."""
+    return max(1, -(-ROTATE_BYTES // int(bytes_per_launch)))
+
+
+def launch_groups_us(torch, fns, groups, settle_s=0.1):
+    """Per-launch microseconds of `groups` groups of LAUNCHES back-to-back
+    launches cycling through `fns` (one callable per buffer set), each group
+    between one pair of HIP events on the current stream."""
+    st = torch.cuda.current_stream()
+    k = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(LAUNCHES):
+            fns[k % len(fns)]()
+            k += 1
+        torch.cuda.synchronize()
+    us = []
+    for _ in range(groups):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(LAUNCHES):
+            fns[k % len(fns)]()
+            k += 1
+        b.record(st)
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3 / LAUNCHES)
+    return us
+
+
+def launch_time_us(np, torch, fns, groups, settle_s=0.1):
+    """(median, minimum) of launch_groups_us."""
+    us = launch_groups_us(torch, fns, groups, settle_s)
+    return float(np.median(us)), float(np.min(us))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -42,10 +88,10 @@ def parse():
                          "sustained HBM load the chip's power controller lowers the clocks and "
                          "takes tens of ms to settle, and the timed steps should see the settled "
                          "state")
-    ap.add_argument("--kernel-samples", type=int, default=20,
-                    help="after the timed steps, run this many more steps with a HIP event pair "
-                         "around every kernel (on the launch stream); per-kernel times are the "
-                         "medians of these samples, whatever --steps is")
+    ap.add_argument("--kernel-groups", type=int, default=10,
+                    help="after the timed steps, time each kernel in this many groups of "
+                         f"{LAUNCHES} back-to-back launches over rotating buffer sets; the "
+                         "per-kernel figures are the medians over the groups, whatever --steps is")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.6)
@@ -167,13 +213,9 @@ def main():
     ]
     step_bytes = sum(k[2] for k in kernels)
 
-    def step(events=None):
-        for i, (_, fn, _) in enumerate(kernels):
-            if events is not None:
-                events[i][0].record()
+    def step():
+        for _, fn, _ in kernels:
             fn()
-            if events is not None:
-                events[i][1].record()
 
     settle_steps = 0
     t_settle = time.perf_counter()
@@ -186,10 +228,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # The timed steps carry no events (an event pair costs the command
-    # processor a few microseconds; around every kernel of every step it
-    # would add ~3% to the step).
-    torch.cuda.synchronize()
+    # The timed steps: no events inside.
     t_start = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -197,20 +236,37 @@ def main():
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
 
-    # Per-kernel times: a separate pass of --kernel-samples steps with a HIP
-    # event pair around every kernel, on the stream the kernels run on; the
-    # median of the samples.  Each kernel keeps its place in the step (it
-    # reads what the previous kernel did not write), so the last-level cache
-    # holds none of its input.
-    E = max(1, args.kernel_samples)
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in kernels] for _ in range(E)]
-    for s in range(E):
-        step(ev[s])
+    # Per-kernel times (after the timed steps): each kernel alone, LAUNCHES
+    # back-to-back launches per group, rotating over buffer sets so that no
+    # launch finds its data in the last-level cache (set 0 is the step's own).
+    def rotation(i):
+        name, fn, nbytes = kernels[i]
+        k = n_sets(nbytes)
+        if k == 1:
+            return [fn]
+        if i == 0:                      # K1: other ranks' shards, own outputs
+            outs = [(e(Sw, T.int8), e(Sw // Bw, T.float32)) for _ in range(k - 1)]
+            return [fn] + [lambda r=r, o=o: zpq.quant_i8(layer[r * Sw:(r + 1) * Sw], Bw, out=o)
+                           for r, o in zip(range(1, k), outs)]
+        if i == 3:                      # K4: copies of the hop-1 receive buffer
+            sets = [(recv1_c.clone(), recv1_s.clone(), e(chunk // 2, T.uint8),
+                     e(chunk // Bg, T.float32)) for _ in range(k - 1)]
+            return [fn] + [lambda q=q: zpq.qgz_dequant_reduce_requant_i4(
+                q[0], q[1], L, chunk, Bg, out=(q[2], q[3])) for q in sets]
+        if i == 4:                      # K5: copies of the hop-2 receive buffer
+            sets = [(recv2_c.clone(), recv2_s.clone(), e(Sg, T.float16)) for _ in range(k - 1)]
+            return [fn] + [lambda q=q: zpq.qgz_dequant_reduce_requant_i4(
+                q[0], q[1], N, Sg, Bg, out_dtype=T.float16, divisor=float(W), out=q[2])
+                for q in sets]
+        raise AssertionError(f"no rotation for kernel {i}")
+    G = max(1, args.kernel_groups)
+    per_kernel = []
+    for i in range(len(kernels)):
+        fns = rotation(i)
+        med, mn = launch_time_us(np, torch, fns, G)
+        per_kernel.append((med, mn, len(fns)))
+        del fns
     torch.cuda.synchronize()
-    samples_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(E)]
-                  for i in range(len(kernels))]
-    per_kernel_ms = [float(np.median(v)) for v in samples_ms]
 
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -233,13 +289,12 @@ def main():
                 traffic = t.get("bytes_per_launch", {})
 
     rows = []
-    for (name, _, nbytes), ms, smp in zip(kernels, per_kernel_ms, samples_ms):
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        rows.append({"kernel": name, "bytes": nbytes, "us": round(ms * 1e3, 2),
-                     "us_mean": round(float(np.mean(smp)) * 1e3, 2),
-                     "us_min": round(float(np.min(smp)) * 1e3, 2),
+    for (name, _, nbytes), (med, mn, nset) in zip(kernels, per_kernel):
+        gbs = nbytes / med / 1e3
+        rows.append({"kernel": name, "bytes": nbytes, "us": round(med, 2),
+                     "us_min": round(mn, 2), "buffer_sets": nset,
                      "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
-    dom = max(range(len(rows)), key=lambda i: per_kernel_ms[i])
+    dom = max(range(len(rows)), key=lambda i: per_kernel[i][0])
     dk = rows[dom]
     tr = traffic.get(dk["kernel"].split(" ")[0])
     roofline = {"bound": "hbm", "kernel": dk["kernel"], "achieved": dk["GBps"],
@@ -264,8 +319,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_steps": settle_steps,
-        "kernel_times": f"median of {E} HIP event pairs per kernel on the launch stream, in a "
-                        f"pass of {E} steps after the timed ones",
+        "kernel_times": f"per-launch time of {LAUNCHES} back-to-back launches between one HIP "
+                        f"event pair, median of {G} groups, rotating buffer sets (>= "
+                        f"{ROTATE_BYTES >> 20} MiB between reuses), after the timed steps",
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -413,97 +469,101 @@ def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):
             "error": "RMS(y - exact mean) / RMS(exact mean), fp64 reference"}
 
 
-def per_config(np, torch, zpq, synth, reps=50, settle_s=0.2):
-    """Every kernel at every workload size, one launch at a time: before each
-    timed launch a read-only pass over 1 GiB of scratch evicts the 256 MB
-    last-level cache (reads leave no dirty lines behind to be written back
-    during the timed kernel); each launch is bracketed by HIP events on its
-    stream; median and minimum over `reps` launches after a settle phase.
-    Inputs are the workloads' generators; the receive buffers of the hop
-    kernels are filled by the send-side kernels (timing needs realistic codes,
-    not oracle values: parity at these sizes is the GPU tests' job)."""
+def per_config(np, torch, zpq, synth, groups=10):
+    """Every kernel at every workload size, alone: kernel time as everywhere
+    in this file (LAUNCHES back-to-back launches per HIP event pair, median
+    over `groups`), each launch on its own buffer set among enough copies
+    that ROTATE_BYTES pass between two uses of one.  Inputs are the
+    workloads' generators; the receive buffers of the hop kernels are filled
+    by the send-side kernels (timing needs realistic codes, not oracle
+    values: parity at these sizes is the GPU tests' job)."""
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     T = torch
-    st = torch.cuda.current_stream()
-    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     rows = []
+    e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
 
-    def timed(label, fn, nbytes):
-        def evict():
-            scratch.max()
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < settle_s:
-            for _ in range(5):
-                evict()
-                fn()
-            torch.cuda.synchronize()
-        us = []
-        for _ in range(reps):
-            evict()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            fn()
-            e1.record(st)
-            torch.cuda.synchronize()
-            us.append(e0.elapsed_time(e1) * 1e3)
-        med = float(np.median(us))
+    def timed(label, nbytes, make):
+        """make(i) -> a callable launching on buffer set i (set 0 may reuse inputs)."""
+        fns = [make(i) for i in range(n_sets(nbytes))]
+        med, mn = launch_time_us(np, torch, fns, groups)
         rows.append({"kernel": label, "bytes": int(nbytes), "us_median": round(med, 2),
-                     "us_min": round(float(min(us)), 2),
+                     "us_min": round(mn, 2), "buffer_sets": len(fns),
                      "GBps": round(nbytes / med / 1e3, 1),
                      "frac_of_peak": round(nbytes / med / 1e3 / HBM_PEAK_GBS, 4)})
-        print(f"[per-config] {label}: {med:.1f} us, {nbytes / med / 1e3:.0f} GB/s",
-              file=sys.stderr, flush=True)
+        print(f"[per-config] {label}: {med:.2f} us, {nbytes / med / 1e3:.0f} GB/s "
+              f"({len(fns)} buffer sets)", file=sys.stderr, flush=True)
+        del fns
+        torch.cuda.empty_cache()
 
-    e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
+    def copy_of(t, i):
+        return t if i == 0 else t.clone()
+
     # c1: qwZ round trip, 2^20 fp16, B = 256 (launch-bound)
     c = synth.QWZ_ROUNDTRIP
     n, B = c["n"], c["block"]
     x = torch.from_numpy(synth.qwz_roundtrip()).to(dev)
-    cc, cs, y = e(n, T.int8), e(n // B, T.float32), e(n, T.float16)
+    cc, cs = zpq.quant_i8(x, B)
     nb = n * 2 + n + n // B * 4
-    timed("c1 K1 quant_i8 2^20 fp16 B=256", lambda: zpq.quant_i8(x, B, out=(cc, cs), stream=st), nb)
-    timed("c1 K2 dequant_i8 2^20 -> fp16", lambda: zpq.dequant_i8(cc, cs, B, out=y, stream=st), nb)
-    del x, cc, cs, y
+
+    def c1_quant(i):
+        xi, o = copy_of(x, i), (e(n, T.int8), e(n // B, T.float32))
+        return lambda: zpq.quant_i8(xi, B, out=o)
+
+    def c1_dequant(i):
+        ci, si, y = copy_of(cc, i), copy_of(cs, i), e(n, T.float16)
+        return lambda: zpq.dequant_i8(ci, si, B, out=y)
+    timed("c1 K1 quant_i8 2^20 fp16 B=256", nb, c1_quant)
+    timed("c1 K2 dequant_i8 2^20 -> fp16", nb, c1_dequant)
+    del x, cc, cs
     # c2: qwZ on the h8192 layer, 16 ranks
     c = synth.QWZ_LAYER
     n, B, W = c["n"], c["block"], c["world"]
     S = n // W
     layer = torch.from_numpy(synth.qwz_layer()).to(dev)
-    sc, ss = e(S, T.int8), e(S // B, T.float32)
-    gc, gs, y = e(n, T.int8), e(n // B, T.float32), e(n, T.float16)
-    zpq.quant_i8(layer, B, out=(gc, gs), stream=st)
-    timed("c2 K1 quant_i8 shard 50.3M fp16 B=256",
-          lambda: zpq.quant_i8(layer[:S], B, out=(sc, ss), stream=st), S * 3 + S // B * 4)
-    timed("c2 K2 dequant_i8 gathered 805M -> fp16",
-          lambda: zpq.dequant_i8(gc, gs, B, out=y, stream=st), n * 3 + n // B * 4)
-    del layer, sc, ss, gc, gs, y
+
+    def c2_quant(i):                    # rank i's shard
+        o = (e(S, T.int8), e(S // B, T.float32))
+        return lambda: zpq.quant_i8(layer[i * S:(i + 1) * S], B, out=o)
+    timed("c2 K1 quant_i8 shard 50.3M fp16 B=256", S * 3 + S // B * 4, c2_quant)
+    gc, gs = zpq.quant_i8(layer, B)
+    del layer
+    y = e(n, T.float16)
+    timed("c2 K2 dequant_i8 gathered 805M -> fp16", n * 3 + n // B * 4,
+          lambda i: (lambda: zpq.dequant_i8(gc, gs, B, out=y)))
+    del gc, gs, y
     # c3: qgZ hop 1, bf16 2^28, L = 8, N = 4, B = 128
     c = synth.QGZ_HOP1
     n, B, L, N = c["n"], c["block"], c["L"], c["N"]
     chunk = n // L
     g = torch.from_numpy(synth.qgz_hop1()).view(T.bfloat16).to(dev)
     c1, s1 = e(n // 2, T.uint8), e(n // B, T.float32)
-    c2, s2 = e(chunk // 2, T.uint8), e(chunk // B, T.float32)
-    timed("c3 K3 reorder_quant_i4 2^28 bf16 L=8 N=4 B=128",
-          lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1), stream=st),
-          n * 2 + n // 2 + n // B * 4)
+    timed("c3 K3 reorder_quant_i4 2^28 bf16 L=8 N=4 B=128", n * 2 + n // 2 + n // B * 4,
+          lambda i: (lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1))))
+    del g
+
+    def c3_hop1(i):
+        ci, si = copy_of(c1, i), copy_of(s1, i)
+        o = (e(chunk // 2, T.uint8), e(chunk // B, T.float32))
+        return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, L, chunk, B, out=o)
     timed("c3 K4 hop-1 8 x 2^25 -> INT4",
-          lambda: zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B, out=(c2, s2), stream=st),
-          L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4)
-    del g, c1, s1, c2, s2
+          L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4, c3_hop1)
+    del c1, s1
     # c4: qgZ hop 2, 16 sources x 2^24, bf16 average
     c = synth.QGZ_HOP2
     K, chunk, B = c["sources"], c["chunk"], c["block"]
     src = torch.from_numpy(np.concatenate([synth.qgz_hop2_source(i) for i in range(K)])).to(dev)
     ic, isc = zpq.qgz_reorder_quant_i4(src, 1, 1, B)
     del src
-    y = e(chunk, T.bfloat16)
-    timed("c4 K5 hop-2 16 x 2^24 -> bf16 average",
-          lambda: zpq.qgz_dequant_reduce_requant_i4(ic, isc, K, chunk, B, out_dtype=T.bfloat16,
-                                                    divisor=c["divisor"], out=y, stream=st),
-          K * (chunk // 2 + chunk // B * 4) + chunk * 2)
-    del ic, isc, y
+
+    def c4_hop2(i):
+        ci, si, yv = copy_of(ic, i), copy_of(isc, i), e(chunk, T.bfloat16)
+        return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, K, chunk, B,
+                                                         out_dtype=T.bfloat16,
+                                                         divisor=c["divisor"], out=yv)
+    timed("c4 K5 hop-2 16 x 2^24 -> bf16 average", K * (chunk // 2 + chunk // B * 4) + chunk * 2,
+          c4_hop2)
+    del ic, isc
     # c5: fused qgZ on the 138B-model layer gradient, L = 8, N = 48, B = 64
     c = synth.QGZ_FUSED
     n, B, L, N = c["n"], c["block"], c["L"], c["N"]
@@ -511,33 +571,39 @@ def per_config(np, torch, zpq, synth, reps=50, settle_s=0.2):
     S, chunk = n // W, n // L
     g = torch.from_numpy(synth.qgz_fused()).to(dev)
     c1, s1 = e(n // 2, T.uint8), e(n // B, T.float32)
-    c2, s2 = e(chunk // 2, T.uint8), e(chunk // B, T.float32)
-    y = e(S, T.float16)
-    timed("c5 K3 reorder_quant_i4 1.06G fp16 L=8 N=48 B=64",
-          lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1), stream=st),
-          n * 2 + n // 2 + n // B * 4)
+    timed("c5 K3 reorder_quant_i4 1.06G fp16 L=8 N=48 B=64", n * 2 + n // 2 + n // B * 4,
+          lambda i: (lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1))))
+    del g
+    c2, s2 = zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B)
+
+    def c5_hop1(i):
+        ci, si = copy_of(c1, i), copy_of(s1, i)
+        o = (e(chunk // 2, T.uint8), e(chunk // B, T.float32))
+        return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, L, chunk, B, out=o)
     timed("c5 K4 hop-1 8 x 132M -> INT4",
-          lambda: zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B, out=(c2, s2), stream=st),
-          L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4)
-    timed("c5 K5 hop-2 48 x 2.75M -> fp16 average",
-          lambda: zpq.qgz_dequant_reduce_requant_i4(c2, s2, N, S, B, out_dtype=T.float16,
-                                                    divisor=float(W), out=y, stream=st),
-          N * (S // 2 + S // B * 4) + S * 2)
-    return {"per_config": rows, "timing": f"median of {reps} single launches, HIP events, "
-            "1 GiB read-only pass before each launch, 200 ms settle per kernel",
+          L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4, c5_hop1)
+    del c1, s1
+
+    def c5_hop2(i):
+        ci, si, yv = copy_of(c2, i), copy_of(s2, i), e(S, T.float16)
+        return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, N, S, B, out_dtype=T.float16,
+                                                         divisor=float(W), out=yv)
+    timed("c5 K5 hop-2 48 x 2.75M -> fp16 average", N * (S // 2 + S // B * 4) + S * 2, c5_hop2)
+    return {"per_config": rows,
+            "timing": f"per-launch time of {LAUNCHES} back-to-back launches between one HIP event "
+                      f"pair, median of {groups} groups; launches rotate over buffer sets so that "
+                      f">= {ROTATE_BYTES >> 20} MiB pass between two uses of one",
             "peak_GBps": HBM_PEAK_GBS}
 
 
-def patterns(np, torch, zpq, synth, reps=50, settle_s=0.2):
+def patterns(np, torch, zpq, synth, settle_s=0.1):
     """Each kernel at each workload size beside its bare access pattern, and
     the streaming ceilings.  The pattern kernels (bench_patterns.hip) issue
     the same per-lane loads and stores as the kernel -- widths, cache hints,
     lane layout, tiles per lane, sources in flight, grid, slice reorder --
-    with XOR in place of the arithmetic.  Timing as --per-config: a 1 GiB
-    read-only pass before every launch (the last-level cache holds nothing of
-    the launch's data), HIP events on the launch stream, medians of `reps`
-    launches; kernel and pattern alternate in rounds of 10 so that both see
-    the same clock state."""
+    with XOR in place of the arithmetic.  Timing as --per-config (back-to-back
+    launches over rotating buffer sets); kernel and pattern alternate in runs
+    of 5 groups, twice, so that both see the same clock state."""
     import ctypes
     path = os.path.join(ROOT, "libbench_patterns.so")
     if not os.path.exists(path):
@@ -559,47 +625,37 @@ def patterns(np, torch, zpq, synth, reps=50, settle_s=0.2):
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
     null = ctypes.c_void_p(0)
     e = lambda n, dt: torch.empty(n, dtype=dt, device=dev)
-    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def ok(rc):
         if rc != 0:
             raise RuntimeError(f"pattern launch failed ({rc})")
 
-    def time_pair(fns):
-        """Median microseconds of each function, evicting before each launch."""
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < settle_s:
-            for f in fns:
-                scratch.max()
-                f()
-            torch.cuda.synchronize()
-        us = [[] for _ in fns]
-        for _ in range(reps // 10):
-            for k, f in enumerate(fns):
-                ev = []
-                for _ in range(10):
-                    scratch.max()
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record(st)
-                    f()
-                    b.record(st)
-                    ev.append((a, b))
-                torch.cuda.synchronize()
-                us[k] += [a.elapsed_time(b) * 1e3 for a, b in ev]
+    def time_pair(makes, nbytes):
+        """Median per-launch microseconds of each of the given launch families
+        (make(i) -> callable on buffer set i), alternating 5 groups each, twice."""
+        fam = [[m(i) for i in range(n_sets(nbytes))] for m in makes]
+        us = [[] for _ in fam]
+        for _ in range(2):
+            for k, fns in enumerate(fam):
+                us[k] += launch_groups_us(torch, fns, 5, settle_s)
+        del fam
         return [float(np.median(u)) for u in us]
 
     rows = []
 
-    def row(label, nbytes, kfn, pfn):
-        k_us, p_us = time_pair([kfn, pfn])
+    def row(label, nbytes, make_k, make_p):
+        k_us, p_us = time_pair([make_k, make_p], nbytes)
         rows.append({"kernel": label, "bytes": int(nbytes), "kernel_us": round(k_us, 2),
                      "pattern_us": round(p_us, 2),
                      "kernel_frac_of_peak": round(nbytes / k_us / 1e3 / HBM_PEAK_GBS, 4),
                      "pattern_frac_of_peak": round(nbytes / p_us / 1e3 / HBM_PEAK_GBS, 4),
                      "kernel_over_pattern": round(k_us / p_us, 3)})
-        print(f"[patterns] {label}: kernel {k_us:.1f} us, pattern {p_us:.1f} us",
+        print(f"[patterns] {label}: kernel {k_us:.2f} us, pattern {p_us:.2f} us",
               file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+
+    cp = lambda t, i: t if i == 0 else t.clone()
 
     def receive_shape(c, K, fl):
         if not fl:
@@ -607,66 +663,86 @@ def patterns(np, torch, zpq, synth, reps=50, settle_s=0.2):
         waves16 = (c + 16 * 64 - 1) // (16 * 64)
         return (8, 4) if waves16 < 8 * 4 * cus else (16, 2)
 
-    # ceilings: 1 GiB streams
+    # ceilings: 1 GiB streams (no reuse within the last-level cache)
     nb = 1 << 30
     a, b = e(nb // 4, T.float32), e(nb // 4, T.float32)
     a.fill_(1.0)
     sink = e(256, T.int32)
     ceil = {}
-    for name, f, moved in (("read", lambda: ok(P.pat_read(ptr(a), nb, ptr(sink), S_)), nb),
-                           ("write", lambda: ok(P.pat_write(ptr(b), nb, S_)), nb),
-                           ("copy", lambda: ok(P.pat_copy(ptr(a), ptr(b), nb, S_)), 2 * nb)):
-        (us,) = time_pair([f])
+    for name, f, moved in (("read", lambda i: (lambda: ok(P.pat_read(ptr(a), nb, ptr(sink), S_))), nb),
+                           ("write", lambda i: (lambda: ok(P.pat_write(ptr(b), nb, S_))), nb),
+                           ("copy", lambda i: (lambda: ok(P.pat_copy(ptr(a), ptr(b), nb, S_))),
+                            2 * nb)):
+        (us,) = time_pair([f], moved)
         ceil[name] = {"bytes": moved, "us": round(us, 2), "GBps": round(moved / us / 1e3, 1),
                       "frac_of_peak": round(moved / us / 1e3 / HBM_PEAK_GBS, 4)}
         print(f"[patterns] {name} ceiling: {moved / us / 1e3:.0f} GB/s", file=sys.stderr, flush=True)
     del a, b
 
-    # c2: qwZ on the h8192 layer
+    # c2: qwZ on the h8192 layer (buffer set i: rank i's shard)
     c = synth.QWZ_LAYER
     n, B, W = c["n"], c["block"], c["world"]
     S = n // W
     layer = torch.from_numpy(synth.qwz_layer()).to(dev)
-    sc, ss, pc, ps = e(S, T.int8), e(S // B, T.float32), e(S, T.int8), e(S // B, T.float32)
-    row("c2 K1 quant_i8 shard 50.3M fp16 B=256", S * 3 + S // B * 4,
-        lambda: zpq.quant_i8(layer[:S], B, out=(sc, ss), stream=st),
-        lambda: ok(P.pat_quant_i8(ptr(layer), S, ptr(pc), ptr(ps), S_)))
-    gc, gs, y, py = e(n, T.int8), e(n // B, T.float32), e(n, T.float16), e(n, T.float16)
-    zpq.quant_i8(layer, B, out=(gc, gs), stream=st)
-    del layer, sc, ss, pc, ps
+
+    def k1_kernel(i):
+        o = (e(S, T.int8), e(S // B, T.float32))
+        return lambda: zpq.quant_i8(layer[i * S:(i + 1) * S], B, out=o)
+
+    def k1_pattern(i):
+        o = (e(S, T.int8), e(S // B, T.float32))
+        return lambda: ok(P.pat_quant_i8(ptr(layer[i * S:]), S, ptr(o[0]), ptr(o[1]), S_))
+    row("c2 K1 quant_i8 shard 50.3M fp16 B=256", S * 3 + S // B * 4, k1_kernel, k1_pattern)
+    gc, gs = zpq.quant_i8(layer, B)
+    del layer
+    y, py = e(n, T.float16), e(n, T.float16)
     row("c2 K2 dequant_i8 gathered 805M -> fp16", n * 3 + n // B * 4,
-        lambda: zpq.dequant_i8(gc, gs, B, out=y, stream=st),
-        lambda: ok(P.pat_dequant_i8(ptr(gc), ptr(gs), n, ptr(py), S_)))
+        lambda i: (lambda: zpq.dequant_i8(gc, gs, B, out=y)),
+        lambda i: (lambda: ok(P.pat_dequant_i8(ptr(gc), ptr(gs), n, ptr(py), S_))))
     del gc, gs, y, py
 
-    def qgz_rows(tag, g, dt_bytes, L, N, B, out_dt, fl2_label, fl1_label, k3_label):
+    def qgz_rows(g, dt_bytes, L, N, B, out_dt, fl2_label, fl1_label, k3_label):
         n = g.numel()
         W = L * N
         S, chunk = n // W, n // L
         c1, s1, p1, q1 = e(n // 2, T.uint8), e(n // B, T.float32), e(n // 2, T.uint8), e(n // B, T.float32)
         row(k3_label, n * dt_bytes + n // 2 + n // B * 4,
-            lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1), stream=st),
-            lambda: ok(P.pat_reorder_quant_i4(ptr(g), n, L, N, B, ptr(p1), ptr(q1), S_)))
-        c2, s2, p2, q2 = (e(chunk // 2, T.uint8), e(chunk // B, T.float32), e(chunk // 2, T.uint8),
-                          e(chunk // B, T.float32))
+            lambda i: (lambda: zpq.qgz_reorder_quant_i4(g, L, N, B, out=(c1, s1))),
+            lambda i: (lambda: ok(P.pat_reorder_quant_i4(ptr(g), n, L, N, B, ptr(p1), ptr(q1), S_))))
+        del p1, q1
+        c2, s2 = zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B)
         epl, pf = receive_shape(chunk, L, False)
+
+        def h1_kernel(i):
+            ci, si = cp(c1, i), cp(s1, i)
+            o = (e(chunk // 2, T.uint8), e(chunk // B, T.float32))
+            return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, L, chunk, B, out=o)
+
+        def h1_pattern(i):
+            ci, si = cp(c1, i), cp(s1, i)
+            o = (e(chunk // 2, T.uint8), e(chunk // B, T.float32))
+            return lambda: ok(P.pat_receive(ptr(ci), ptr(si), L, chunk, B, ptr(o[0]), ptr(o[1]),
+                                            null, epl, pf, S_))
         row(fl1_label, L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4,
-            lambda: zpq.qgz_dequant_reduce_requant_i4(c1, s1, L, chunk, B, out=(c2, s2), stream=st),
-            lambda: ok(P.pat_receive(ptr(c1), ptr(s1), L, chunk, B, ptr(p2), ptr(q2), null, epl, pf,
-                                     S_)))
+            h1_kernel, h1_pattern)
         if fl2_label:
-            yv, pv = e(S, out_dt), e(S, out_dt)
-            epl, pf = receive_shape(S, N, True)
-            row(fl2_label, N * (S // 2 + S // B * 4) + S * 2,
-                lambda: zpq.qgz_dequant_reduce_requant_i4(c2, s2, N, S, B, out_dtype=out_dt,
-                                                          divisor=float(W), out=yv, stream=st),
-                lambda: ok(P.pat_receive(ptr(c2), ptr(s2), N, S, B, null, null, ptr(pv), epl, pf,
-                                         S_)))
+            epl2, pf2 = receive_shape(S, N, True)
+
+            def h2_kernel(i):
+                ci, si, yv = cp(c2, i), cp(s2, i), e(S, out_dt)
+                return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, N, S, B, out_dtype=out_dt,
+                                                                 divisor=float(W), out=yv)
+
+            def h2_pattern(i):
+                ci, si, yv = cp(c2, i), cp(s2, i), e(S, out_dt)
+                return lambda: ok(P.pat_receive(ptr(ci), ptr(si), N, S, B, null, null, ptr(yv),
+                                                epl2, pf2, S_))
+            row(fl2_label, N * (S // 2 + S // B * 4) + S * 2, h2_kernel, h2_pattern)
 
     # c3: qgZ hop 1
     c = synth.QGZ_HOP1
     g = torch.from_numpy(synth.qgz_hop1()).view(T.bfloat16).to(dev)
-    qgz_rows("c3", g, 2, c["L"], c["N"], c["block"], None, None,
+    qgz_rows(g, 2, c["L"], c["N"], c["block"], None, None,
              "c3 K4 hop-1 8 x 2^25 -> INT4", "c3 K3 reorder_quant_i4 2^28 bf16 L=8 N=4 B=128")
     del g
     # c4: qgZ hop 2, 16 x 2^24 -> bf16
@@ -675,26 +751,34 @@ def patterns(np, torch, zpq, synth, reps=50, settle_s=0.2):
     src = torch.from_numpy(np.concatenate([synth.qgz_hop2_source(i) for i in range(K)])).to(dev)
     ic, isc = zpq.qgz_reorder_quant_i4(src, 1, 1, B)
     del src
-    yv, pv = e(chunk, T.bfloat16), e(chunk, T.bfloat16)
     epl, pf = receive_shape(chunk, K, True)
+
+    def c4_kernel(i):
+        ci, si, yv = cp(ic, i), cp(isc, i), e(chunk, T.bfloat16)
+        return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, K, chunk, B, out_dtype=T.bfloat16,
+                                                         divisor=c["divisor"], out=yv)
+
+    def c4_pattern(i):
+        ci, si, yv = cp(ic, i), cp(isc, i), e(chunk, T.bfloat16)
+        return lambda: ok(P.pat_receive(ptr(ci), ptr(si), K, chunk, B, null, null, ptr(yv), epl, pf,
+                                        S_))
     row("c4 K5 hop-2 16 x 2^24 -> bf16 average", K * (chunk // 2 + chunk // B * 4) + chunk * 2,
-        lambda: zpq.qgz_dequant_reduce_requant_i4(ic, isc, K, chunk, B, out_dtype=T.bfloat16,
-                                                  divisor=c["divisor"], out=yv, stream=st),
-        lambda: ok(P.pat_receive(ptr(ic), ptr(isc), K, chunk, B, null, null, ptr(pv), epl, pf, S_)))
-    del ic, isc, yv, pv
+        c4_kernel, c4_pattern)
+    del ic, isc
     # c5: fused qgZ
     c = synth.QGZ_FUSED
     g = torch.from_numpy(synth.qgz_fused()).to(dev)
-    qgz_rows("c5", g, 2, c["L"], c["N"], c["block"], T.float16,
+    qgz_rows(g, 2, c["L"], c["N"], c["block"], T.float16,
              "c5 K5 hop-2 48 x 2.75M -> fp16 average", "c5 K4 hop-1 8 x 132M -> INT4",
              "c5 K3 reorder_quant_i4 1.06G fp16 L=8 N=48 B=64")
     return {"patterns": rows, "ceilings_1GiB": ceil,
-            "timing": f"median of {reps} single launches per kernel and per pattern, HIP events, "
-                      "1 GiB read-only pass before each launch, kernel and pattern alternating in "
-                      "rounds of 10", "peak_GBps": HBM_PEAK_GBS}
+            "timing": f"per-launch time of {LAUNCHES} back-to-back launches between one HIP event "
+                      f"pair; launches rotate over buffer sets (>= {ROTATE_BYTES >> 20} MiB between "
+                      "two uses of one); kernel and pattern alternate in runs of 5 groups, twice; "
+                      "median of the 10 groups", "peak_GBps": HBM_PEAK_GBS}
 
 
-def blocking_study(np, torch, zpq, synth, reps=20):
+def blocking_study(np, torch, zpq, synth):
     """INT8 weight quantization with one scale per tensor against one scale
     per block (the summary page's ablation: non-blocked quantization of the
     weights hurt, block-based did not).  Reconstruction error of both on the
@@ -727,23 +811,21 @@ def blocking_study(np, torch, zpq, synth, reps=20):
               f"{r['block_256']['rel_rms_err']}", file=sys.stderr, flush=True)
     x = torch.from_numpy(cases["layer_shard"]).to(dev)
     n = x.numel()
-    codes = torch.empty(n, dtype=torch.int8, device=dev)
-    sc = torch.empty(n // 256, dtype=torch.float32, device=dev)
-    s1 = torch.empty(1, dtype=torch.float32, device=dev)
-    st = torch.cuda.current_stream()
     timing = {}
-    for label, fn, nbytes in (
-            ("block_256", lambda: zpq.quant_i8(x, 256, out=(codes, sc), stream=st), 3 * n + n // 64),
-            ("per_tensor", lambda: zpq.quant_i8_tensor(x, out=(codes, s1), stream=st), 3 * n)):
-        for _ in range(3):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(reps):
-            fn()
-        e1.record(st)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+    for label, nbytes, make in (
+            ("block_256", 3 * n + n // 64,
+             lambda i: (lambda xi=x if i == 0 else x.clone(),
+                        o=(torch.empty(n, dtype=torch.int8, device=dev),
+                           torch.empty(n // 256, dtype=torch.float32, device=dev)):
+                        zpq.quant_i8(xi, 256, out=o))),
+            ("per_tensor", 3 * n,
+             lambda i: (lambda xi=x if i == 0 else x.clone(),
+                        o=(torch.empty(n, dtype=torch.int8, device=dev),
+                           torch.empty(1, dtype=torch.float32, device=dev)):
+                        zpq.quant_i8_tensor(xi, out=o)))):
+        fns = [make(i) for i in range(n_sets(nbytes))]
+        us, _ = launch_time_us(np, torch, fns, 10)
+        del fns
         timing[label] = {"us_per_call": round(us, 2),
                          "effective_GBps": round(nbytes / us / 1e3, 1)}
     return {"study": "INT8 weight quantization: per-tensor scale vs per-block scales",
