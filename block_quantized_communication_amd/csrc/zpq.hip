@@ -18,15 +18,20 @@
 // Every kernel streams HBM once (the per-tensor quantizer twice: it needs the
 // tensor's maximum before the first code): wide vector loads, one quantization block per
 // aligned group of BLOCK/EPL lanes of a wave64 (EPL = elements per lane),
-// the block absmax reduced with DPP lane permutes, the division done as a
-// correctly rounded multiply-and-correct sequence, codes packed in registers
-// and written with 64/128-bit stores.  No LDS and no MFMA: the work is an
-// elementwise map with a segmented reduction, bound by HBM bandwidth (and,
-// for the hop-receive kernel, by VALU issue).
+// the block absmax reduced with DPP lane permutes, the division done without
+// the IEEE divide (a multiply and one residual correction for 16-bit inputs,
+// one binary64 product for binary32 operands, both equal to the IEEE
+// quotient where it matters), codes packed in registers and written with
+// 64/128-bit stores.  No LDS and no MFMA: the work is an elementwise map with a
+// segmented reduction, bound by HBM bandwidth (and, for the hop-receive
+// kernel, by VALU issue).
 //
 // Bit-exactness: every result equals the plain definition (IEEE binary32
 // operations rounded to nearest even, division included) for all finite
-// inputs.  Denormals are kept (the gfx950 default f32/f16 denormal mode).
+// inputs, except that a NaN the definition produces (a sum meeting +inf and
+// -inf) may differ in sign and payload, and requantized blocks whose sums are
+// not all finite are unspecified.  Denormals are kept (the gfx950 default
+// f32/f16 denormal mode).
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
