@@ -709,17 +709,24 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
 // ---------------------------------------------------------------------------
 // K4: qgZ dequantize -> fp32 reduce in source order -> INT4 requant or average.
 //
-// Per source and element: d = fl32(q * s) computed as fma(u, s, -8s) with
-// u = q + 8 in 0..15 (the nibble with its top bit flipped, converted by
-// v_cvt_f32_ubyte): the FMA rounds the exact (u - 8) * s once, which is
-// fl32(q * s).  -8s is exact unless 8|s| overflows (|s| > FLT_MAX/8); then that
-// source's terms are -inf, and since all elements of a lane share each
-// source's scale, every sum of the lane ends -inf or NaN (no term is ever
-// +inf: a valid -8s keeps |(u - 8) * s| <= 8|s| finite).  The lane therefore
-// checks one sum at the end and, if it is not finite, recomputes with q * s
-// directly, which is the definition itself and so also right when true sums
-// overflow.  The sum is acc = fl32(acc + d), starting at +0, sources in order
-// 0..K-1.
+// Per source and element: d = fl32(q * s), as ONE rounding of an exact
+// expression in u = q + 8 in 0..15 (the nibble with its top bit flipped):
+//  * INT4 output (hop 1): u converted by v_cvt_f32_ubyte, d = fma(u, s, -8s);
+//  * float output (hop 2): one XOR flips the top bit of a dword's eight
+//    nibbles, a mask puts two of them into the two 16-bit halves of a
+//    register, and v_fma_mix_f32 reads a half as the fp16 number u * 2^-24:
+//    d = fma(u * 2^-24, s * 2^24, -8s).
+// (Measured per launch shape: the mixed-precision form is faster for the
+// float-output launches, the conversion form for the INT4-output ones.)
+// The scaled constants are exact unless they overflow (|s| > FLT_MAX/8 for
+// -8s, |s| > FLT_MAX/2^24 for s * 2^24); then that source's term is +-inf or
+// NaN (u * inf, 0 * inf or inf - inf) for every element of the lane, since
+// all of them share the source's scale, while a term made with finite
+// constants is finite.  A non-finite sum never becomes finite again, so the
+// lane checks one sum at the end and, if it is not finite, recomputes with
+// q * s directly, which is the definition itself and so also right when true
+// sums overflow.  The sum is acc = fl32(acc + d), starting at +0, sources in
+// order 0..K-1.
 template <int EPL>
 struct SrcCodes {
     static constexpr int W = EPL / 8;     // dwords of nibbles per lane and source
@@ -774,8 +781,40 @@ __device__ __forceinline__ float cvt_ubyte(uint32_t x) {
     return r;
 }
 
-template <int EPL>
+// fl32(h * s24 + c) where h is the 16-bit half H of x read as an fp16
+// number: one v_fma_mix_f32.
+template <int H>
+__device__ __forceinline__ float fma_mix_half(uint32_t x, float s24, float c) {
+    float r;
+    if constexpr (H == 0)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+            : "=v"(r) : "v"(x), "v"(s24), "v"(c));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+            : "=v"(r) : "v"(x), "v"(s24), "v"(c));
+    return r;
+}
+
+// acc[e] = fl32(acc[e] + fl32(q_e * s)) for the EPL elements of one source;
+// MIX selects the v_fma_mix_f32 form (see above).
+template <int EPL, bool MIX>
 __device__ __forceinline__ void accumulate(float (&acc)[EPL], const SrcCodes<EPL>& d) {
+    if constexpr (MIX) {
+        const float s24 = d.s * 0x1p24f;
+        const float c8 = d.s * -8.0f;
+#pragma unroll
+        for (int i = 0; i < SrcCodes<EPL>::W; ++i) {
+            const uint32_t x = d.w[i] ^ 0x88888888u;          // every nibble q -> q + 8
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // nibble k (element 8i+k) in the low half, nibble k+4 in the high half
+                const uint32_t h = (x >> (4 * k)) & 0x000F000Fu;
+                acc[8 * i + k] = acc[8 * i + k] + fma_mix_half<0>(h, s24, c8);
+                acc[8 * i + k + 4] = acc[8 * i + k + 4] + fma_mix_half<1>(h, s24, c8);
+            }
+        }
+        return;
+    }
     const float s = d.s;
     const float c = s * -8.0f;
 #pragma unroll
@@ -888,22 +927,22 @@ __device__ __forceinline__ void reduce_tile(
         for (; i0 + 2 * PF <= K; i0 += PF) {
 #pragma unroll
             for (int k = 0; k < PF; ++k) {
-                accumulate<EPL>(acc, buf[k]);
+                accumulate<EPL, (OUT >= 0)>(acc, buf[k]);
                 src_load(buf[k], i0 + PF + k);
             }
         }
 #pragma unroll
-        for (int k = 0; k < PF; ++k) accumulate<EPL>(acc, buf[k]);
+        for (int k = 0; k < PF; ++k) accumulate<EPL, (OUT >= 0)>(acc, buf[k]);
         for (int i = i0 + PF; i < K; ++i) {          // fewer than PF left
             SrcCodes<EPL> d;
             src_load(d, i);
-            accumulate<EPL>(acc, d);
+            accumulate<EPL, (OUT >= 0)>(acc, d);
         }
     } else {
         for (int i = 0; i < K; ++i) {
             SrcCodes<EPL> d;
             src_load(d, i);
-            accumulate<EPL>(acc, d);
+            accumulate<EPL, (OUT >= 0)>(acc, d);
         }
     }
     // An overflowed -8s leaves every sum of the lane -inf or NaN (see above):
