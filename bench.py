@@ -116,6 +116,10 @@ def parse():
                     help="time every kernel at every workload size beside its bare access pattern "
                          "(the same loads and stores without the arithmetic, from "
                          "bench_patterns.hip) and the read / write / copy ceilings")
+    ap.add_argument("--valu-rates", action="store_true",
+                    help="measure the vector ALU's issue rate per instruction kind and per "
+                         "per-element sequence of the hop-receive loop (register-only kernels "
+                         "from bench_patterns.hip)")
     ap.add_argument("--study", choices=["hop-count", "blocking"], default=None,
                     help="run an error study instead of the throughput benchmark")
     ap.add_argument("--copy-probe", action="store_true",
@@ -154,6 +158,9 @@ def main():
         return
     if args.patterns:
         print(json.dumps(patterns(np, torch, zpq, synth)), flush=True)
+        return
+    if args.valu_rates:
+        print(json.dumps(valu_rates(np, torch)), flush=True)
         return
 
     torch.cuda.set_device(0)
@@ -655,15 +662,28 @@ def patterns(np, torch, zpq, synth, settle_s=0.1):
 
     rows = []
 
+    def read_stream(nbytes):
+        """A plain read stream of (about) `nbytes` -- the streaming ceiling at
+        the kernel's own size, where the launch's ramp-up and drain weigh as
+        much as they do for the kernel -- on its own buffer sets."""
+        n16 = -(-int(nbytes) // (16 * 2 * 256)) * (2 * 256)
+        bufs = [e(n16 * 4, T.float32).fill_(1.0) for _ in range(n_sets(n16 * 16))]
+        return n16 * 16, [(lambda b=b: ok(P.pat_read(ptr(b), n16 * 16, ptr(sink), S_))) for b in bufs]
+
     def row(label, nbytes, make_k, make_p):
         k_us, p_us = time_pair([make_k, make_p], nbytes)
+        rb, fns = read_stream(nbytes)
+        r_us = float(np.median(launch_groups_us(torch, fns, 10, settle_s)))
+        del fns
         rows.append({"kernel": label, "bytes": int(nbytes), "kernel_us": round(k_us, 2),
                      "pattern_us": round(p_us, 2),
                      "kernel_frac_of_peak": round(nbytes / k_us / 1e3 / HBM_PEAK_GBS, 4),
                      "pattern_frac_of_peak": round(nbytes / p_us / 1e3 / HBM_PEAK_GBS, 4),
-                     "kernel_over_pattern": round(k_us / p_us, 3)})
-        print(f"[patterns] {label}: kernel {k_us:.2f} us, pattern {p_us:.2f} us",
-              file=sys.stderr, flush=True)
+                     "kernel_over_pattern": round(k_us / p_us, 3),
+                     "read_stream_bytes": rb, "read_stream_us": round(r_us, 2),
+                     "read_stream_frac_of_peak": round(rb / r_us / 1e3 / HBM_PEAK_GBS, 4)})
+        print(f"[patterns] {label}: kernel {k_us:.2f} us, pattern {p_us:.2f} us, "
+              f"read stream of the same size {r_us:.2f} us", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
     cp = lambda t, i: t if i == 0 else t.clone()
@@ -783,10 +803,83 @@ def patterns(np, torch, zpq, synth, settle_s=0.1):
              "c5 K5 hop-2 48 x 2.75M -> fp16 average", "c5 K4 hop-1 8 x 132M -> INT4",
              "c5 K3 reorder_quant_i4 1.06G fp16 L=8 N=48 B=64")
     return {"patterns": rows, "ceilings_1GiB": ceil,
+            "read_stream": "per row, a plain read stream (16-byte non-temporal loads, two tiles "
+                           "per lane) of the kernel's algorithmic bytes, timed the same way",
             "timing": f"per-launch time of {LAUNCHES} back-to-back launches between one HIP event "
                       f"pair; launches rotate over buffer sets (>= {ROTATE_BYTES >> 20} MiB between "
                       "two uses of one); kernel and pattern alternate in runs of 5 groups, twice; "
                       "median of the 10 groups", "peak_GBps": HBM_PEAK_GBS}
+
+
+VALU_KINDS = [
+    ("v_add_f32", "op"), ("v_mul_f32", "op"), ("v_fma_f32", "op"), ("v_cvt_f32_ubyte1", "op"),
+    ("v_cvt_off_f32_i4", "op"), ("v_cvt_f32_i32 (SDWA byte select)", "op"), ("v_and_b32", "op"),
+    ("v_lshrrev_b32", "op"), ("v_bitop3_b32", "op"), ("v_perm_b32", "op"), ("v_max3_f32", "op"),
+    ("v_fma_mix_f32", "op"), ("v_cvt_pk_f32_fp8 (two results)", "op"), ("v_mul_f64", "op"),
+    ("cvt_f32_ubyte + fma + add (the receive loop's form)", "seq"),
+    ("cvt_f32_ubyte + mul + add", "seq"),
+    ("cvt_off_f32_i4 (SDWA byte select) + mul + add", "seq"),
+    ("fma_mix (16-bit operand) + add", "seq"),
+    ("mov + mul + add (no conversion)", "seq"),
+]
+
+
+def valu_rates(np, torch, waves_per_simd=(4, 8), iters=2000):
+    """Issue rate of the vector ALU per instruction kind, and per element for
+    the per-element instruction sequences a dequantize-and-add loop can use.
+    Register-only kernels (bench_patterns.hip): 8 independent chains per
+    lane, nothing but the measured instructions in the loop.  One launch per
+    kind and occupancy, HIP events around it, best of 3 (each launch runs
+    for a millisecond or more, so the event overhead is negligible)."""
+    import ctypes
+    path = os.path.join(ROOT, "libbench_patterns.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libbench_patterns.so is missing: run __graft_entry__.build()")
+    P = ctypes.CDLL(path)
+    P.pat_valu.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                           ctypes.c_void_p]
+    P.pat_valu_instr_per_step.argtypes = [ctypes.c_int]
+    nk = P.pat_valu_kinds()
+    if nk != len(VALU_KINDS):
+        raise RuntimeError(f"bench_patterns.hip has {nk} VALU kinds, bench.py names {len(VALU_KINDS)}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    simds = cus * 4
+    st = torch.cuda.current_stream()
+    rows = []
+    for wps in waves_per_simd:
+        wgs = simds * wps // 4                      # 4 waves per 256-thread workgroup
+        out = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+        for k, (name, kind) in enumerate(VALU_KINDS):
+            ips = P.pat_valu_instr_per_step(k)
+            rc = P.pat_valu(k, wgs, 10, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"VALU kernel {k} failed to launch ({rc})")
+            torch.cuda.synchronize()
+            best = None
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                P.pat_valu(k, wgs, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+                b.record(st)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b)
+                best = ms if best is None else min(best, ms)
+            steps_per_simd = wps * iters * 32          # inner steps (one element each) per SIMD
+            ns = best * 1e6
+            row = {"kind": name, "what": kind, "waves_per_simd": wps, "ms": round(best, 4),
+                   "instr_per_ns_per_simd": round(steps_per_simd * ips / ns, 4),
+                   "cycles_per_instr_at_2p4GHz": round(ns * 2.4 / (steps_per_simd * ips), 3)}
+            if kind == "seq":
+                row["cycles_per_element_at_2p4GHz"] = round(ns * 2.4 / steps_per_simd, 3)
+            rows.append(row)
+            print(f"[valu] {wps} waves/SIMD  {name}: {row['cycles_per_instr_at_2p4GHz']} cycles/instr",
+                  file=sys.stderr, flush=True)
+        del out
+    return {"valu_rates": rows, "simds": simds,
+            "note": "a wave64 instruction on a 16-lane SIMD takes 4 cycles when issued alone; "
+                    "fewer cycles per instruction mean two waves' instructions issued together"}
 
 
 def blocking_study(np, torch, zpq, synth):

@@ -9,7 +9,11 @@
 //    stores (widths, cache hints, lane layout, tiles per lane, sources in
 //    flight, grid shape, the slice reorder of the qgZ quantizer) with the
 //    arithmetic replaced by XOR -- what the kernel's memory traffic alone
-//    costs.  Their outputs are meaningless.
+//    costs.  Their outputs are meaningless;
+//  * VALU issue rates: one instruction kind (or one per-element instruction
+//    sequence of the hop-receive loop) repeated on registers, eight
+//    independent chains per lane, no memory traffic inside the loop -- what
+//    the vector ALU sustains per SIMD for that kind.
 //
 // Every entry point takes device pointers and a hipStream_t, checks nothing
 // beyond what its caller (bench.py) guarantees (whole tiles / blocks, the
@@ -233,6 +237,139 @@ __global__ __launch_bounds__(kThreads) void k_pat_receive(
     }
 }
 
+// ---------------------------------------------------------------------------
+// VALU issue rates.  Each kernel runs `iters` iterations of 4 x 8 copies of
+// one instruction (or one per-element sequence) on 8 independent register
+// chains per lane; an empty asm statement on the inputs each iteration keeps
+// the compiler from hoisting anything.  The instructions are written as asm
+// so that exactly the named encoding issues.  One store per lane at the end.
+#define ZPQB_VALU1(name, text)                                                             \
+    __global__ __launch_bounds__(kThreads) void name(uint32_t* out, int iters, float b) {  \
+        float a[8];                                                                        \
+        for (int i = 0; i < 8; ++i) a[i] = threadIdx.x * 0.001f + i;                        \
+        for (int it = 0; it < iters; ++it) {                                                \
+            asm volatile("" : "+v"(b));                                                     \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                 \
+                _Pragma("unroll") for (int i = 0; i < 8; ++i)                               \
+                    asm volatile(text : "+v"(a[i]) : "v"(b));                               \
+            }                                                                               \
+        }                                                                                   \
+        float t = 0.0f;                                                                     \
+        for (int i = 0; i < 8; ++i) t += a[i];                                              \
+        out[blockIdx.x * kThreads + threadIdx.x] = __float_as_uint(t);                      \
+    }
+ZPQB_VALU1(k_valu_add, "v_add_f32 %0, %0, %1")
+ZPQB_VALU1(k_valu_mul, "v_mul_f32 %0, %0, %1")
+ZPQB_VALU1(k_valu_fma, "v_fma_f32 %0, %0, %1, %1")
+ZPQB_VALU1(k_valu_cvt_ubyte, "v_cvt_f32_ubyte1 %0, %0")
+ZPQB_VALU1(k_valu_cvt_off, "v_cvt_off_f32_i4 %0, %0")
+ZPQB_VALU1(k_valu_cvt_sdwa,
+           "v_cvt_f32_i32_sdwa %0, sext(%0) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1")
+ZPQB_VALU1(k_valu_and, "v_and_b32 %0, %0, %1")
+ZPQB_VALU1(k_valu_shift, "v_lshrrev_b32 %0, 4, %0")
+ZPQB_VALU1(k_valu_bitop3, "v_bitop3_b32 %0, %0, %1, %1 bitop3:0x6c")
+ZPQB_VALU1(k_valu_perm, "v_perm_b32 %0, %0, %1, %1")
+ZPQB_VALU1(k_valu_max3, "v_max3_f32 %0, %0, %1, %1")
+ZPQB_VALU1(k_valu_fma_mix, "v_fma_mix_f32 %0, %0, %1, %1")
+// two-result conversion (two fp8 bytes to two floats) and a binary64 multiply
+__global__ __launch_bounds__(kThreads) void k_valu_cvt_pk_fp8(uint32_t* out, int iters, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    uint32_t x[8];
+    f32x2 p[8];
+    for (int i = 0; i < 8; ++i) x[i] = threadIdx.x * 0x9E3779B9u + i;
+    for (int it = 0; it < iters; ++it) {
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(x[i]));
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) {
+            _Pragma("unroll") for (int i = 0; i < 8; ++i)
+                asm volatile("v_cvt_pk_f32_fp8 %0, %1" : "=v"(p[i]) : "v"(x[i]));
+        }
+    }
+    float t = b;
+    for (int i = 0; i < 8; ++i) t += p[i].x + p[i].y;
+    out[blockIdx.x * kThreads + threadIdx.x] = __float_as_uint(t);
+}
+__global__ __launch_bounds__(kThreads) void k_valu_mul_f64(uint32_t* out, int iters, float b) {
+    double d[8];
+    double db = (double)b;
+    for (int i = 0; i < 8; ++i) d[i] = threadIdx.x * 0.001 + i;
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" : "+v"(db));
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) {
+            _Pragma("unroll") for (int i = 0; i < 8; ++i)
+                asm volatile("v_mul_f64 %0, %0, %1" : "+v"(d[i]) : "v"(db));
+        }
+    }
+    double t = 0.0;
+    for (int i = 0; i < 8; ++i) t += d[i];
+    out[blockIdx.x * kThreads + threadIdx.x] = __float_as_uint((float)t);
+}
+
+// Per-element sequences of a dequantize-and-add loop: a nibble (in byte 1 of
+// w) becomes a float, is scaled and added to the element's sum.
+#define ZPQB_VALU_SEQ(name, body)                                                          \
+    __global__ __launch_bounds__(kThreads) void name(uint32_t* out, int iters, float b) {  \
+        float a[8];                                                                        \
+        uint32_t w[8];                                                                     \
+        const float c = -8.0f * b;                                                         \
+        for (int i = 0; i < 8; ++i) {                                                      \
+            a[i] = 0.0f;                                                                    \
+            w[i] = (threadIdx.x * 0x9E3779B9u + i) & 0x0F0F0F0Fu;                            \
+        }                                                                                   \
+        for (int it = 0; it < iters; ++it) {                                                \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(w[i]));    \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                 \
+                _Pragma("unroll") for (int i = 0; i < 8; ++i) {                             \
+                    float u;                                                                \
+                    body                                                                    \
+                }                                                                           \
+            }                                                                               \
+        }                                                                                   \
+        float t = 0.0f;                                                                     \
+        for (int i = 0; i < 8; ++i) t += a[i];                                              \
+        out[blockIdx.x * kThreads + threadIdx.x] = __float_as_uint(t);                      \
+    }
+// the receive loop's form: byte conversion, rounding FMA (u - 8) * s, add
+ZPQB_VALU_SEQ(k_seq_cvt_fma_add,
+              asm volatile("v_cvt_f32_ubyte1 %0, %1" : "=v"(u) : "v"(w[i]));
+              asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(u) : "v"(b), "v"(c));
+              asm volatile("v_add_f32 %0, %0, %1" : "+v"(a[i]) : "v"(u));)
+// the same with a plain multiply (needs a signed value; shown for its rate)
+ZPQB_VALU_SEQ(k_seq_cvt_mul_add,
+              asm volatile("v_cvt_f32_ubyte1 %0, %1" : "=v"(u) : "v"(w[i]));
+              asm volatile("v_mul_f32 %0, %0, %1" : "+v"(u) : "v"(b));
+              asm volatile("v_add_f32 %0, %0, %1" : "+v"(a[i]) : "v"(u));)
+// signed conversion of a nibble with an SDWA byte select, multiply, add
+ZPQB_VALU_SEQ(k_seq_sdwa_mul_add,
+              asm volatile("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD "
+                           "src0_sel:BYTE_1" : "=v"(u) : "v"(w[i]));
+              asm volatile("v_mul_f32 %0, %0, %1" : "+v"(u) : "v"(b));
+              asm volatile("v_add_f32 %0, %0, %1" : "+v"(a[i]) : "v"(u));)
+// mixed-precision FMA on a 16-bit operand (conversion folded in), add
+ZPQB_VALU_SEQ(k_seq_fmamix_add,
+              asm volatile("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]"
+                           : "=v"(u) : "v"(w[i]), "v"(b), "v"(c));
+              asm volatile("v_add_f32 %0, %0, %1" : "+v"(a[i]) : "v"(u));)
+// no conversion at all: copy, multiply, add (a lower bound for any form)
+ZPQB_VALU_SEQ(k_seq_mov_mul_add,
+              asm volatile("v_mov_b32 %0, %1" : "=v"(u) : "v"(w[i]));
+              asm volatile("v_mul_f32 %0, %0, %1" : "+v"(u) : "v"(b));
+              asm volatile("v_add_f32 %0, %0, %1" : "+v"(a[i]) : "v"(u));)
+
+typedef void (*valu_kernel_t)(uint32_t*, int, float);
+struct ValuKind {
+    valu_kernel_t fn;
+    int instr_per_step;     // instructions per chain and inner step
+};
+const ValuKind kValuKinds[] = {
+    {k_valu_add, 1}, {k_valu_mul, 1}, {k_valu_fma, 1}, {k_valu_cvt_ubyte, 1},
+    {k_valu_cvt_off, 1}, {k_valu_cvt_sdwa, 1}, {k_valu_and, 1}, {k_valu_shift, 1},
+    {k_valu_bitop3, 1}, {k_valu_perm, 1}, {k_valu_max3, 1}, {k_valu_fma_mix, 1},
+    {k_valu_cvt_pk_fp8, 1}, {k_valu_mul_f64, 1},
+    {k_seq_cvt_fma_add, 3}, {k_seq_cvt_mul_add, 3}, {k_seq_sdwa_mul_add, 3},
+    {k_seq_fmamix_add, 2}, {k_seq_mov_mul_add, 3},
+};
+constexpr int kNumValuKinds = sizeof(kValuKinds) / sizeof(kValuKinds[0]);
+
 inline unsigned grid_for(int64_t units, int64_t per_wg) {
     return (unsigned)((units + per_wg - 1) / per_wg);
 }
@@ -311,6 +448,23 @@ int pat_receive(const void* in_codes, const void* in_scales, int32_t K, int64_t 
                            c, block, oc, os, ov);
     else
         return (int)hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// VALU issue-rate kernel `kind` (0 .. pat_valu_kinds() - 1) on `wgs`
+// workgroups of 256 threads, `iters` iterations; `out` holds wgs * 256 words.
+// Instructions issued per wave: iters * 32 * instr_per_step.
+int pat_valu_kinds(void) { return kNumValuKinds; }
+
+int pat_valu_instr_per_step(int kind) {
+    return (kind >= 0 && kind < kNumValuKinds) ? kValuKinds[kind].instr_per_step : 0;
+}
+
+int pat_valu(int kind, int32_t wgs, int32_t iters, void* out, void* st) {
+    if (kind < 0 || kind >= kNumValuKinds || wgs <= 0 || iters <= 0)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(kValuKinds[kind].fn, dim3((unsigned)wgs), dim3(kThreads), 0,
+                       (hipStream_t)st, (uint32_t*)out, iters, 1.0001f);
     return hipGetLastError();
 }
 
