@@ -576,16 +576,17 @@ __global__ __launch_bounds__(kThreads) void k_tensor_codes(const void* __restric
 
 // ---------------------------------------------------------------------------
 // K2: qwZ INT8 dequantize into fp32 / fp16 / bf16.
-template <int OT, int EPL, bool NT>
-__device__ __forceinline__ void store_out(void* __restrict__ y, int64_t e, const float (&v)[EPL]) {
+template <int OT>
+struct OutBytes { static constexpr int v = OT == ZPQ_F32 ? 4 : 2; };
+
+// EPL values in the output type, as EPL * size / 16 16-byte vectors.
+template <int OT, int EPL>
+__device__ __forceinline__ void pack_out(const float (&v)[EPL], u32x4 (&o)[EPL * OutBytes<OT>::v / 16]) {
     if constexpr (OT == ZPQ_F32) {
-        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<float*>(y) + e);
 #pragma unroll
         for (int k = 0; k < EPL / 4; ++k)
-            st_stream<NT>(
-                u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
-                      __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])},
-                dst + k);
+            o[k] = u32x4{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                         __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
     } else {
         uint32_t h[EPL / 2];
 #pragma unroll
@@ -602,12 +603,47 @@ __device__ __forceinline__ void store_out(void* __restrict__ y, int64_t e, const
             else
                 h[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(ab, bf16x2));
         }
-        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + e);
 #pragma unroll
-        for (int k = 0; k < EPL / 8; ++k)
-            st_stream<NT>(u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]},
-                                        dst + k);
+        for (int k = 0; k < EPL / 8; ++k) o[k] = u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
     }
+}
+
+// The lane's EPL output values (elements e .. e+EPL-1) as consecutive 16-byte stores.
+template <int OT, int EPL, bool NT>
+__device__ __forceinline__ void store_out(void* __restrict__ y, int64_t e, const float (&v)[EPL]) {
+    constexpr int V = EPL * OutBytes<OT>::v / 16;
+    u32x4 o[V];
+    pack_out<OT, EPL>(v, o);
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(y) + e * OutBytes<OT>::v);
+#pragma unroll
+    for (int k = 0; k < V; ++k) st_stream<NT>(o[k], dst + k);
+}
+
+// The same values written by the whole wave as V coalesced 1 KB stores: the
+// lanes' vectors pass through the wave's own LDS slice (V * 64 vectors,
+// lane-major in, store-major out), so store k of lane L writes the wave's
+// 16-byte vector 64k + L.  Needs every lane of the wave active, holding
+// elements wbase + EPL*lane .. (wbase = the wave's first element).  With more
+// than one vector per lane the plain stores of neighbouring lanes are V*16
+// bytes apart and each store instruction covers its 64 lanes' share of
+// V KB; these cover 1 KB each.
+template <int OT, int EPL, bool NT>
+__device__ __forceinline__ void store_out_wave(void* __restrict__ y, int64_t e, const float (&v)[EPL],
+                                               u32x4* __restrict__ slice) {
+    constexpr int V = EPL * OutBytes<OT>::v / 16;
+    u32x4 o[V];
+    pack_out<OT, EPL>(v, o);
+    const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+    for (int k = 0; k < V; ++k) slice[lane * V + k] = o[k];
+    __builtin_amdgcn_wave_barrier();        // the reads below take other lanes' writes
+#pragma unroll
+    for (int k = 0; k < V; ++k) o[k] = slice[k * 64 + lane];
+    __builtin_amdgcn_wave_barrier();        // a later use of the slice comes after these reads
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(y) + (e - (int64_t)lane * EPL) *
+                                                                    OutBytes<OT>::v);
+#pragma unroll
+    for (int k = 0; k < V; ++k) st_stream<NT>(o[k], dst + k * 64 + lane);
 }
 
 template <int OT, int BLOCK, int EPL, int U>
@@ -712,12 +748,14 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
 // Per source and element: d = fl32(q * s), as ONE rounding of an exact
 // expression in u = q + 8 in 0..15 (the nibble with its top bit flipped):
 //  * INT4 output (hop 1): u converted by v_cvt_f32_ubyte, d = fma(u, s, -8s);
-//  * float output (hop 2): one XOR flips the top bit of a dword's eight
+//  * float output (hop 2, wide launches): one XOR flips the top bit of a dword's eight
 //    nibbles, a mask puts two of them into the two 16-bit halves of a
 //    register, and v_fma_mix_f32 reads a half as the fp16 number u * 2^-24:
 //    d = fma(u * 2^-24, s * 2^24, -8s).
 // (Measured per launch shape: the mixed-precision form is faster for the
-// float-output launches, the conversion form for the INT4-output ones.)
+// float-output launches with 16 or more elements per lane, the conversion
+// form for the INT4-output ones; at 8 per lane the two trade places from one
+// box to the next, and the conversion form stays.)
 // The scaled constants are exact unless they overflow (|s| > FLT_MAX/8 for
 // -8s, |s| > FLT_MAX/2^24 for s * 2^24); then that source's term is +-inf or
 // NaN (u * inf, 0 * inf or inf - inf) for every element of the lane, since
@@ -882,19 +920,28 @@ template <int BLOCK, int EPL, int OUT, int PF>
 __device__ __forceinline__ void reduce_tile(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
-    void* __restrict__ out_vals, float divisor, double rdiv, float thr, int64_t e);
+    void* __restrict__ out_vals, float divisor, double rdiv, float thr, int64_t e,
+    u32x4* __restrict__ slice);
+
+// 16-byte vectors per lane of the float output; with two or more, the
+// output goes through an LDS slice of V * 64 vectors per wave.
+template <int OUT, int EPL>
+struct OutVectors { static constexpr int v = OUT < 0 ? 0 : EPL * (OUT == ZPQ_F32 ? 4 : 2) / 16; };
 
 template <int BLOCK, int EPL, int OUT /* -1: INT4, else a zpq_dtype */, int PF>
 __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
     void* __restrict__ out_vals, float divisor, double rdiv, float thr, uint32_t nvb) {
+    constexpr int V = OutVectors<OUT, EPL>::v;
+    __shared__ u32x4 stage[V >= 2 ? kThreads / 64 : 1][V >= 2 ? V * 64 : 1];
+    u32x4* const slice = &stage[V >= 2 ? threadIdx.x / 64 : 0][0];
     for (uint32_t k = blockIdx.x; k < nvb; k += gridDim.x) {
     const uint32_t vb = tile_of<ZPQ_XCD_REDUCE>(k, nvb);
         const int64_t e = ((int64_t)vb * kThreads + threadIdx.x) * EPL;
         if (e < c)                 // whole quantization blocks leave together
             reduce_tile<BLOCK, EPL, OUT, PF>(in_codes, in_scales, K, c, out_codes, out_scales,
-                                             out_vals, divisor, rdiv, thr, e);
+                                             out_vals, divisor, rdiv, thr, e, slice);
     }
 }
 
@@ -902,7 +949,8 @@ template <int BLOCK, int EPL, int OUT, int PF>
 __device__ __forceinline__ void reduce_tile(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
-    void* __restrict__ out_vals, float divisor, double rdiv, float thr, int64_t e) {
+    void* __restrict__ out_vals, float divisor, double rdiv, float thr, int64_t e,
+    u32x4* __restrict__ slice) {
     constexpr int G = BLOCK / EPL;
     const int64_t cstride = c / 2, sstride = c / BLOCK;
     const uint32_t coff = (uint32_t)(e / 2), soff = (uint32_t)(e / BLOCK);   // c < 2^32
@@ -927,22 +975,22 @@ __device__ __forceinline__ void reduce_tile(
         for (; i0 + 2 * PF <= K; i0 += PF) {
 #pragma unroll
             for (int k = 0; k < PF; ++k) {
-                accumulate<EPL, (OUT >= 0)>(acc, buf[k]);
+                accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, buf[k]);
                 src_load(buf[k], i0 + PF + k);
             }
         }
 #pragma unroll
-        for (int k = 0; k < PF; ++k) accumulate<EPL, (OUT >= 0)>(acc, buf[k]);
+        for (int k = 0; k < PF; ++k) accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, buf[k]);
         for (int i = i0 + PF; i < K; ++i) {          // fewer than PF left
             SrcCodes<EPL> d;
             src_load(d, i);
-            accumulate<EPL, (OUT >= 0)>(acc, d);
+            accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, d);
         }
     } else {
         for (int i = 0; i < K; ++i) {
             SrcCodes<EPL> d;
             src_load(d, i);
-            accumulate<EPL, (OUT >= 0)>(acc, d);
+            accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, d);
         }
     }
     // An overflowed -8s leaves every sum of the lane -inf or NaN (see above):
@@ -991,7 +1039,14 @@ __device__ __forceinline__ void reduce_tile(
                 y[k] = (fabsf(acc[k]) >= thr || acc[k] == 0.0f) ? div_f64(acc[k], rdiv)
                                                                  : acc[k] / divisor;
         }
-        store_out<OUT, EPL, ZPQ_NTS_REDUCE>(out_vals, e, y);
+        if constexpr (OutVectors<OUT, EPL>::v >= 2) {
+            if (__builtin_amdgcn_read_exec() == ~0ull)      // a whole wave: coalesced stores
+                store_out_wave<OUT, EPL, ZPQ_NTS_REDUCE>(out_vals, e, y, slice);
+            else
+                store_out<OUT, EPL, ZPQ_NTS_REDUCE>(out_vals, e, y);
+        } else {
+            store_out<OUT, EPL, ZPQ_NTS_REDUCE>(out_vals, e, y);
+        }
     }
 }
 

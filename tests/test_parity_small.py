@@ -182,14 +182,17 @@ def test_dequant_reduce_average_overflowing_sums(out, divisor):
     assert_equal_nan_aware(got, ref, out, "values")
 
 
-@pytest.mark.parametrize("out", ["bf16", "f32"])
-def test_dequant_reduce_average_long_chunk(out):
+@pytest.mark.parametrize("out", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("tail", [0, 128 * 3])
+def test_dequant_reduce_average_long_chunk(out, tail):
     """A chunk long enough for the hop-2 launch with 16 elements per lane
-    (short chunks take 8 per lane): 2^23 + 2^16 elements, 3 sources."""
-    rng = np.random.default_rng(77)
-    K, block, chunk = 3, 128, (1 << 23) + (1 << 16)
+    (short chunks take 8 per lane): 2^23 + 2^16 elements, 3 sources; with a
+    tail, the last wave is partly empty and writes its outputs lane by lane
+    (whole waves write theirs as coalesced 1 KB stores)."""
+    rng = np.random.default_rng(77 + tail)
+    K, block, chunk = 3, 128, (1 << 23) + (1 << 16) + tail
     codes, s = random_received(rng, K, chunk, block)
-    print(f"dequant_reduce_average long chunk out={out} K={K} chunk={chunk}", flush=True)
+    print(f"dequant_reduce_average long chunk out={out} K={K} chunk={chunk} tail={tail}", flush=True)
     y = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk, block,
                                            out_dtype=torch_dt(out), divisor=3.0)
     ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, out, 3.0)
