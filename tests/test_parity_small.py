@@ -13,7 +13,11 @@ pytestmark = pytest.mark.gpu
 
 DTYPES = ["f32", "f16", "bf16"]
 BLOCKS = [32, 64, 128, 256, 512]
-TILE = 256 * 16 * 2        # elements per workgroup of the quantize kernels
+# Largest workgroup tile of the quantize kernels: fp32 inputs hold 16 elements per
+# lane, two tiles per lane (8192 elements); 16-bit inputs hold 8 per lane (4096).
+# Sizes below are multiples of it plus a ragged tail, so they span several tiles
+# of every element type.
+TILE = 256 * 16 * 2
 
 
 def torch_dt(name):
