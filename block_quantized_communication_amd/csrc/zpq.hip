@@ -22,9 +22,10 @@
 // the IEEE divide (a multiply and one residual correction for 16-bit inputs,
 // one binary64 product for binary32 operands, both equal to the IEEE
 // quotient where it matters), codes packed in registers and written with
-// 64/128-bit stores.  No LDS and no MFMA: the work is an elementwise map with a
+// 64/128-bit stores.  No MFMA: the work is an elementwise map with a
 // segmented reduction, bound by HBM bandwidth (and, for the hop-receive
-// kernel, by VALU issue).
+// kernel, by VALU issue).  LDS only stages a wave's averaged outputs so that
+// they leave as coalesced 1 KB stores.
 //
 // Bit-exactness: every result equals the plain definition (IEEE binary32
 // operations rounded to nearest even, division included) for all finite
