@@ -22,6 +22,13 @@
  *               rounding boundary (k + 1/2) * s, k = 0..Q, both signs, plus x
  *               = a and 64 random |x| <= a: the kernel's code equals
  *               clamp(rint_even(x / s)).
+ *   fastcodes Q T   the same scales and values for the hop-1 requantization's
+ *               faster code route: with a normal scale, r = RN32(1/s) and
+ *               t = fl32(x * r), the code is rint_even(t) unless t lies within
+ *               2^-19 of a half-integer (then, and for scales below 2^-126,
+ *               the binary64 route above): every value that takes the fast
+ *               route gets the definition's code.  Output adds "near K", the
+ *               values sent to the binary64 route.
  *   mean T      divisors d = 1..65536, all powers of two 2^-40..2^40 and
  *               200000 random floats in [2^-20, 2^40]; for each, sums next to
  *               binary32 rounding boundaries of the quotient (16 ulp either
@@ -63,6 +70,26 @@ static float k_code(float x, float s, int q) {
     if (!(s >= 0x1p-126f)) t = fminf(fmaxf(t, -(float)q), (float)q);
     return rintf(t);
 }
+/* the hop-1 requantization's faster route: t = fl32(x * RN32(1/s)) is within
+ * 2^-19 of fl32(x / s) when s is normal and |x| <= 7.0000009 s (the absmax
+ * element included), so rint_even(t) is the code unless t is that close to a
+ * half-integer.  PLANT_NARROW_MARGIN shrinks the margin to 2^-30 (a plausible
+ * mistake) so that the test can show the checker catching it. */
+#ifdef PLANT_NARROW_MARGIN
+#define FAST_MARGIN (0.5f - 0x1p-30f)
+#else
+#define FAST_MARGIN (0.5f - 0x1p-19f)
+#endif
+static float k_code_fast(float x, float s, int q, int* exact_route) {
+    if (!(s >= 0x1p-126f)) { *exact_route = 1; return k_code(x, s, q); }
+    const float r = (float)(1.0 / (double)s);
+    const float t = x * r;
+    const float y = (t + 12582912.0f) - 12582912.0f;   /* rint_even(t), |t| < 2^22 */
+    const float d = t - y;
+    if (fabsf(d) > FAST_MARGIN) { *exact_route = 1; return k_code(x, s, q); }
+    *exact_route = 0;
+    return y;
+}
 /* the definition */
 static float d_code(float x, float s, int q) {
     if (s == 0.0f) return 0.0f;
@@ -80,7 +107,8 @@ static uint64_t sm_next(uint64_t* st) {
     return z ^ (z >> 31);
 }
 
-typedef struct { int t; long long bad, cases; } job_t;
+typedef struct { int t; long long bad, cases, near; } job_t;
+static int g_fast;     /* fastcodes mode: check k_code_fast instead of k_code */
 
 static void* scale_job(void* arg) {
     job_t* j = (job_t*)arg;
@@ -99,7 +127,14 @@ static void* scale_job(void* arg) {
 
 static void check_code(job_t* j, float x, float s) {
     j->cases++;
-    if (k_code(x, s, g_q) != d_code(x, s, g_q)) j->bad++;
+    if (g_fast) {
+        int exact_route = 0;
+        const float c = k_code_fast(x, s, g_q, &exact_route);
+        j->near += exact_route;
+        if (c != d_code(x, s, g_q)) j->bad++;
+    } else if (k_code(x, s, g_q) != d_code(x, s, g_q)) {
+        j->bad++;
+    }
 }
 
 static void* codes_job(void* arg) {
@@ -198,10 +233,11 @@ int main(int argc, char** argv) {
     if (argc < 3) return 2;
     const char* mode = argv[1];
     void* (*fn)(void*) = NULL;
-    if (!strcmp(mode, "scale") || !strcmp(mode, "codes")) {
+    if (!strcmp(mode, "scale") || !strcmp(mode, "codes") || !strcmp(mode, "fastcodes")) {
         if (argc < 4) return 2;
         g_q = atoi(argv[2]);
         g_threads = atoi(argv[3]);
+        g_fast = !strcmp(mode, "fastcodes");
         fn = !strcmp(mode, "scale") ? scale_job : codes_job;
     } else if (!strcmp(mode, "mean")) {
         g_threads = atoi(argv[2]);
@@ -217,12 +253,14 @@ int main(int argc, char** argv) {
         jobs[t].t = t;
         pthread_create(&th[t], NULL, fn, &jobs[t]);
     }
-    long long bad = 0, cases = 0;
+    long long bad = 0, cases = 0, near = 0;
     for (int t = 0; t < g_threads; ++t) {
         pthread_join(th[t], NULL);
         bad += jobs[t].bad;
         cases += jobs[t].cases;
+        near += jobs[t].near;
     }
-    printf("mismatches %lld cases %lld\n", bad, cases);
+    if (g_fast) printf("mismatches %lld cases %lld near %lld\n", bad, cases, near);
+    else printf("mismatches %lld cases %lld\n", bad, cases);
     return 0;
 }

@@ -5,8 +5,11 @@ binary32 division (tests/div_f64_check.c): the scale for every positive
 finite fp32 absmax (qmax 7 and 127), codes for every value within 16 ulp of
 every rounding boundary of quantizer-produced scales in every binade, and
 the average for sums next to rounding boundaries of the quotient across
-65 536 integer, 81 power-of-two and 200 000 random divisors.  A planted
-binary32 product must be caught."""
+65 536 integer, 81 power-of-two and 200 000 random divisors.  Also the
+hop-1 requantization's faster code route (one binary32 product, the
+binary64 route only for values within 2^-19 of a half-integer quotient) on
+the same near-boundary values.  A planted binary32 product and a planted
+too-narrow margin must be caught."""
 import os
 import subprocess
 
@@ -33,6 +36,11 @@ def planted(tmp_path_factory):
     return build(tmp_path_factory, "div_f64_planted", ["-DPLANT_FP32_PRODUCT"])
 
 
+@pytest.fixture(scope="module")
+def planted_margin(tmp_path_factory):
+    return build(tmp_path_factory, "div_f64_planted_margin", ["-DPLANT_NARROW_MARGIN"])
+
+
 def run(exe, *args):
     out = subprocess.run([exe, *args], check=True, capture_output=True, text=True).stdout.split()
     assert out[0] == "mismatches" and out[2] == "cases", out
@@ -53,6 +61,13 @@ def test_codes_next_to_rounding_boundaries(checker, qmax):
     assert bad == 0 and cases > (2 * 10 ** 8 if qmax == 7 else 4 * 10 ** 9), (bad, cases)
 
 
+def test_fast_requant_codes_next_to_rounding_boundaries(checker):
+    """qmax 7 (the hop-1 requantization): every value takes the route the
+    kernel gives it, and each code equals the definition's."""
+    bad, cases = run(checker, "fastcodes", "7", THREADS)
+    assert bad == 0 and cases > 2 * 10 ** 8, (bad, cases)
+
+
 @pytest.mark.slow
 def test_average_next_to_rounding_boundaries(checker):
     bad, cases = run(checker, "mean", THREADS)
@@ -63,3 +78,8 @@ def test_planted_binary32_product_is_caught(planted):
     for args in (("codes", "7", THREADS), ("mean", THREADS)):
         bad, cases = run(planted, *args)
         assert bad > 0, (args, cases)
+
+
+def test_planted_narrow_margin_is_caught(planted_margin):
+    bad, cases = run(planted_margin, "fastcodes", "7", THREADS)
+    assert bad > 0, cases

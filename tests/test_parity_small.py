@@ -203,6 +203,61 @@ def test_dequant_reduce_average_long_chunk(out, tail):
     assert_bits_equal(from_device(y), ref, "values")
 
 
+def requant_near_ties(rng, nblocks, block):
+    """Received chunks whose fp32 sums land on and next to every rounding
+    boundary of the hop-1 requantization.  Per block: element 0 is the block
+    maximum a (so the requantized scale is s = fl32(a/7)); the others are the
+    fp32 values nearest to (k + 1/2) * s, k = 0..6, and their neighbours up to
+    4 ulp away, both signs.  Each value X is a multiple of 2^E (E = the exponent
+    of a minus 27: every fp32 value of magnitude >= a/16 is one) and is built
+    exactly as the sum of 10 sources: source i has scale 2^(E + 3(9 - i)) and
+    code = the i-th base-8 digit of X / 2^E (sign of X), so every product and
+    every partial sum is exact and the kernel's sum is X itself."""
+    K = 10
+    codes = np.zeros((K, nblocks * block), np.int8)
+    scales = np.zeros((K, nblocks), np.float32)
+    for b in range(nblocks):
+        a = np.float32(rng.uniform(1.0, 2.0) * 2.0 ** int(rng.integers(-60, 60)))
+        E = int(np.floor(np.log2(float(a)))) - 27
+        s = np.float32(np.float32(a) / np.float32(7.0))
+        vals = [a]
+        for k in range(7):
+            x0 = np.float32((k + 0.5) * float(s))
+            lo = hi = x0
+            vals += [x0, -x0]
+            for _ in range(4):
+                lo = np.nextafter(lo, np.float32(0))
+                hi = np.nextafter(hi, np.float32(np.inf))
+                vals += [lo, -lo, hi, -hi]
+        vals = vals[:block] + [np.float32(0.0)] * (block - len(vals[:block]))
+        for i in range(K):
+            scales[i, b] = np.float32(2.0 ** (E + 3 * (9 - i)))
+        for j, x in enumerate(vals):
+            m = int(round(abs(float(x)) / 2.0 ** E))
+            assert m * 2.0 ** E == abs(float(x)) and m < 1 << 30
+            sign = -1 if x < 0 else 1
+            for i in range(K):
+                codes[i, b * block + j] = sign * ((m >> (3 * (9 - i))) & 7)
+    packed = ((codes[:, 0::2].astype(np.int32) & 0xF) |
+              ((codes[:, 1::2].astype(np.int32) & 0xF) << 4)).astype(np.uint8)
+    return K, packed.ravel(), scales.ravel()
+
+
+def test_requant_near_ties():
+    """Hop-1 requantization of sums on and next to every rounding boundary
+    (ties to even, values a few ulp either side), in 64 blocks of 128 with
+    maxima across 120 binades: bit-exact against the oracle."""
+    rng = np.random.default_rng(2024)
+    block, nblocks = 128, 64
+    K, codes, s = requant_near_ties(rng, nblocks, block)
+    chunk = nblocks * block
+    print(f"requant near ties K={K} chunk={chunk} block={block}", flush=True)
+    oc, os_ = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk, block)
+    rc, rs = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block)
+    assert_bits_equal(from_device(os_), rs, "scales")
+    assert_bits_equal(from_device(oc), rc, "codes")
+
+
 def test_requant_single_source_is_identity():
     """Hop-1 requantization of one source returns the quantizer's own codes
     and scales (requantization is idempotent)."""
