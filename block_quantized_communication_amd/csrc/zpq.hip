@@ -1011,20 +1011,24 @@ __device__ __forceinline__ void reduce_tile(
         // quantizer's domain: their block's output is unspecified).
         const float m = reduce_abs<true>(acc);
         const float a = __uint_as_float(group_max<G>(__float_as_uint(m)));
-        BlockScale<7, false> bs(a);
+        // The scale s = fl32(a / 7) by the binary64 route (the IEEE operator
+        // below 2^-118, where a/7 is no longer a normal binary32 number).
+        const float s = a >= 0x1p-118f ? div_f64(a, 1.0 / 7.0) : a / 7.0f;
         uint32_t packed[EPL / 8];
         {
-            // Codes from one binary32 product.  With a normal scale s, r =
-            // RN32(1/s) (rounding through binary64 first is harmless for a
-            // quotient) and |x| <= a <= 7.0000009 s, t = fl32(x * r) lies
-            // within 2^-20 of fl32(x / s): unless t is within 2^-19 of a
-            // half-integer, both round to the same integer, so rint_even(t)
+            // Codes from one binary32 product.  With a normal scale s, r
+            // within one ulp of 1/s (the hardware reciprocal refined by one
+            // Newton step) and |x| <= a <= 7.0000009 s, t = fl32(x * r) lies
+            // within 1.4 * 2^-20 of fl32(x / s): unless t is within 2^-19 of
+            // a half-integer, both round to the same integer, so rint_even(t)
             // is the code.  A lane holding a value that close (or a scale
             // below 2^-126) takes the binary64 route for all its codes.
-            // Checked on the CPU for every value within 16 ulp of every
-            // rounding boundary of quantizer-produced scales in every binade.
-            const float r = (float)bs.rd;
-            bool near = !bs.fast;
+            // Checked on the CPU, with both floats next to 1/s, for every
+            // value within 16 ulp of every rounding boundary of
+            // quantizer-produced scales in every binade.
+            const float r0 = __builtin_amdgcn_rcpf(s);
+            const float r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+            bool near = !(s >= 0x1p-126f);
 #pragma unroll
             for (int k = 0; k < EPL / 8; ++k) {
                 uint32_t q[8];
@@ -1039,6 +1043,7 @@ __device__ __forceinline__ void reduce_tile(
                 packed[k] = pack_nibbles(q);
             }
             if (near) {
+                BlockScale<7, false> bs(a);               // the same s, and RN64(1/s)
 #pragma unroll
                 for (int k = 0; k < EPL / 8; ++k) {       // 8 codes at a time: few live registers
                     float v[8];
@@ -1051,7 +1056,7 @@ __device__ __forceinline__ void reduce_tile(
             }
         }
         store_nibbles<EPL, ZPQ_NTS_REDUCE>(out_codes + e / 2, packed);
-        if ((threadIdx.x & (G - 1)) == 0) out_scales[e / BLOCK] = bs.s;
+        if ((threadIdx.x & (G - 1)) == 0) out_scales[e / BLOCK] = s;
     } else {
         // y = fl32(acc / divisor) = div_f64(acc, RN64(1/divisor)) whenever the
         // quotient is a normal binary32 number or overflows, i.e. for

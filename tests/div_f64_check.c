@@ -23,12 +23,15 @@
  *               = a and 64 random |x| <= a: the kernel's code equals
  *               clamp(rint_even(x / s)).
  *   fastcodes Q T   the same scales and values for the hop-1 requantization's
- *               faster code route: with a normal scale, r = RN32(1/s) and
- *               t = fl32(x * r), the code is rint_even(t) unless t lies within
- *               2^-19 of a half-integer (then, and for scales below 2^-126,
- *               the binary64 route above): every value that takes the fast
- *               route gets the definition's code.  Output adds "near K", the
- *               values sent to the binary64 route.
+ *               faster code route: with a normal scale, r either of the two
+ *               floats next to 1/s (the kernel refines the hardware
+ *               reciprocal to one of them) and t = fl32(x * r), the code is
+ *               rint_even(t) unless t lies within 2^-19 of a half-integer
+ *               (then, and for scales below 2^-126, the binary64 route
+ *               above): every value that takes the fast route, with either
+ *               r, gets the definition's code.  Each (value, r) pair is a
+ *               case.  Output adds "near K", the pairs sent to the binary64
+ *               route.
  *   mean T      divisors d = 1..65536, all powers of two 2^-40..2^40 and
  *               200000 random floats in [2^-20, 2^40]; for each, sums next to
  *               binary32 rounding boundaries of the quotient (16 ulp either
@@ -80,9 +83,8 @@ static float k_code(float x, float s, int q) {
 #else
 #define FAST_MARGIN (0.5f - 0x1p-19f)
 #endif
-static float k_code_fast(float x, float s, int q, int* exact_route) {
+static float k_code_fast(float x, float s, float r, int q, int* exact_route) {
     if (!(s >= 0x1p-126f)) { *exact_route = 1; return k_code(x, s, q); }
-    const float r = (float)(1.0 / (double)s);
     const float t = x * r;
     const float y = (t + 12582912.0f) - 12582912.0f;   /* rint_even(t), |t| < 2^22 */
     const float d = t - y;
@@ -128,10 +130,20 @@ static void* scale_job(void* arg) {
 static void check_code(job_t* j, float x, float s) {
     j->cases++;
     if (g_fast) {
-        int exact_route = 0;
-        const float c = k_code_fast(x, s, g_q, &exact_route);
-        j->near += exact_route;
-        if (c != d_code(x, s, g_q)) j->bad++;
+        /* the two floats around 1/s (one float if 1/s is one) */
+        const double rd = 1.0 / (double)s;
+        float r[2];
+        r[0] = (float)rd;
+        r[1] = (double)r[0] == rd ? r[0]
+               : (double)r[0] < rd ? nextafterf(r[0], INFINITY) : nextafterf(r[0], 0.0f);
+        const float want = d_code(x, s, g_q);
+        for (int i = 0; i < 2; ++i) {
+            int exact_route = 0;
+            if (i) j->cases++;
+            const float c = k_code_fast(x, s, r[i], g_q, &exact_route);
+            j->near += exact_route;
+            if (c != want) j->bad++;
+        }
     } else if (k_code(x, s, g_q) != d_code(x, s, g_q)) {
         j->bad++;
     }
