@@ -258,6 +258,34 @@ def test_requant_near_ties():
     assert_bits_equal(from_device(oc), rc, "codes")
 
 
+@pytest.mark.parametrize("waves", [1023, 1025])
+@pytest.mark.parametrize("mode", ["i4", "f16"])
+def test_dequant_reduce_workgroup_shapes(mode, waves):
+    """Receive launches in both workgroup shapes.  The launch uses 4-wave
+    workgroups unless 3-wave ones leave fewer waves on the busiest compute
+    unit; on 256 CUs a launch of 1023 waves takes 4-wave workgroups and one of
+    1025 takes 3-wave ones.  The last wave is partly empty (a ragged tail of
+    3 blocks)."""
+    rng = np.random.default_rng(waves)
+    K = 5
+    block, epl = (128, 32) if mode == "i4" else (64, 8)      # the launch's elements per lane
+    chunk = (waves - 1) * 64 * epl + 3 * block
+    codes, s = random_received(rng, K, chunk, block)
+    print(f"dequant_reduce workgroup shapes mode={mode} waves={waves} chunk={chunk}",
+          flush=True)
+    if mode == "i4":
+        oc, os_ = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk,
+                                                     block)
+        rc, rs = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block)
+        assert_bits_equal(from_device(os_), rs, "scales")
+        assert_bits_equal(from_device(oc), rc, "codes")
+    else:
+        y = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk, block,
+                                               out_dtype=torch_dt("f16"), divisor=5.0)
+        ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, "f16", 5.0)
+        assert_bits_equal(from_device(y), ref, "values")
+
+
 def test_requant_single_source_is_identity():
     """Hop-1 requantization of one source returns the quantizer's own codes
     and scales (requantization is idempotent)."""
