@@ -905,14 +905,16 @@ __device__ __forceinline__ float reduce_abs(const float (&v)[N]) {
     return MAX ? fmaxf(m0, m1) : fminf(m0, m1);
 }
 
-template <int EPL>
+// acc[e] = fl32(acc[e] + q_e * s) with the product formed directly; the
+// first source sets acc[e] = fl32(+0 + q_e * s) (the sum starts at +0).
+template <int EPL, bool FIRST>
 __device__ __forceinline__ void accumulate_direct(float (&acc)[EPL], const SrcCodes<EPL>& d) {
 #pragma unroll
     for (int i = 0; i < SrcCodes<EPL>::W; ++i) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int q = ((int)(d.w[i] << (28 - 4 * k))) >> 28;     // sign-extended nibble
-            acc[8 * i + k] = acc[8 * i + k] + (float)q * d.s;
+            acc[8 * i + k] = (FIRST ? 0.0f : acc[8 * i + k]) + (float)q * d.s;
         }
     }
 }
@@ -947,66 +949,15 @@ __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
     }
 }
 
-template <int BLOCK, int EPL, int OUT, int PF>
-__device__ __forceinline__ void reduce_tile(
-    const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
-    int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
-    void* __restrict__ out_vals, float divisor, double rdiv, float thr, int64_t e,
-    u32x4* __restrict__ slice) {
+// The epilogue of a tile: requantize the sums to INT4 codes and block
+// scales (OUT < 0) or average them and store them as OUT.
+template <int BLOCK, int EPL, int OUT>
+__device__ __forceinline__ void finish_tile(const float (&acc)[EPL], int64_t e,
+                                            uint8_t* __restrict__ out_codes,
+                                            float* __restrict__ out_scales,
+                                            void* __restrict__ out_vals, float divisor,
+                                            double rdiv, float thr, u32x4* __restrict__ slice) {
     constexpr int G = BLOCK / EPL;
-    const int64_t cstride = c / 2, sstride = c / BLOCK;
-    const uint32_t coff = (uint32_t)(e / 2), soff = (uint32_t)(e / BLOCK);   // c < 2^32
-    const uint32_t cbytes = (uint32_t)cstride, sbytes = (uint32_t)(sstride * 4);
-
-    float acc[EPL];
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) acc[k] = 0.0f;
-
-    // Sources in flight.  The steady-state loop refills every slot without a
-    // condition (a whole group of PF sources always remains), so the
-    // compiler can wait for exactly the oldest load instead of all of them.
-    auto src_load = [&](SrcCodes<EPL>& d, int i) {
-        load_src<EPL>(d, in_codes + (int64_t)i * cstride, cbytes, coff,
-                      in_scales + (int64_t)i * sstride, sbytes, soff);
-    };
-    if (K >= PF) {
-        SrcCodes<EPL> buf[PF];
-#pragma unroll
-        for (int k = 0; k < PF; ++k) src_load(buf[k], k);
-        int i0 = 0;
-        for (; i0 + 2 * PF <= K; i0 += PF) {
-#pragma unroll
-            for (int k = 0; k < PF; ++k) {
-                accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, buf[k]);
-                src_load(buf[k], i0 + PF + k);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < PF; ++k) accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, buf[k]);
-        for (int i = i0 + PF; i < K; ++i) {          // fewer than PF left
-            SrcCodes<EPL> d;
-            src_load(d, i);
-            accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, d);
-        }
-    } else {
-        for (int i = 0; i < K; ++i) {
-            SrcCodes<EPL> d;
-            src_load(d, i);
-            accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, d);
-        }
-    }
-    // An overflowed -8s leaves every sum of the lane -inf or NaN (see above):
-    // one sum decides whether the lane is recomputed with q * s directly.
-    if (!(fabsf(acc[0]) <= 3.4028234663852886e38f)) {
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) acc[k] = 0.0f;
-        for (int i = 0; i < K; ++i) {
-            SrcCodes<EPL> d;
-            src_load(d, i);
-            accumulate_direct<EPL>(acc, d);
-        }
-    }
-
     if constexpr (OUT < 0) {
         // Requantize the sums (sums that are not finite lie outside the
         // quantizer's domain: their block's output is unspecified).
@@ -1083,6 +1034,80 @@ __device__ __forceinline__ void reduce_tile(
             store_out<OUT, EPL, ZPQ_NTS_REDUCE>(out_vals, e, y);
         }
     }
+}
+
+template <int BLOCK, int EPL, int OUT, int PF>
+__device__ __forceinline__ void reduce_tile(
+    const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
+    int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
+    void* __restrict__ out_vals, float divisor, double rdiv, float thr, int64_t e,
+    u32x4* __restrict__ slice) {
+    const int64_t cstride = c / 2, sstride = c / BLOCK;
+    const uint32_t coff = (uint32_t)(e / 2), soff = (uint32_t)(e / BLOCK);   // c < 2^32
+    const uint32_t cbytes = (uint32_t)cstride, sbytes = (uint32_t)(sstride * 4);
+
+    float acc[EPL];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) acc[k] = 0.0f;
+
+    // Sources in flight.  The steady-state loop refills every slot without a
+    // condition (a whole group of PF sources always remains), so the
+    // compiler can wait for exactly the oldest load instead of all of them.
+    auto src_load = [&](SrcCodes<EPL>& d, int i) {
+        load_src<EPL>(d, in_codes + (int64_t)i * cstride, cbytes, coff,
+                      in_scales + (int64_t)i * sstride, sbytes, soff);
+    };
+    if (K >= PF) {
+        SrcCodes<EPL> buf[PF];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) src_load(buf[k], k);
+        int i0 = 0;
+        for (; i0 + 2 * PF <= K; i0 += PF) {
+#pragma unroll
+            for (int k = 0; k < PF; ++k) {
+                accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, buf[k]);
+                src_load(buf[k], i0 + PF + k);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PF; ++k) accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, buf[k]);
+        for (int i = i0 + PF; i < K; ++i) {          // fewer than PF left
+            SrcCodes<EPL> d;
+            src_load(d, i);
+            accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, d);
+        }
+    } else {
+        for (int i = 0; i < K; ++i) {
+            SrcCodes<EPL> d;
+            src_load(d, i);
+            accumulate<EPL, (OUT >= 0 && EPL >= 16)>(acc, d);
+        }
+    }
+    // An overflowed -8s leaves every sum of the lane -inf or NaN (see above):
+    // one sum decides whether the lane recomputes its sums with q * s
+    // directly.  For INT4 output the recomputation sets the sums from source
+    // 0 instead of clearing them first: the compiler merges a cleared start
+    // into the usual path as one select per sum (32 instructions per tile,
+    // measured 1-2% of the hop-1 time).  The float-output kernels keep the
+    // cleared start: there the other form measured 3% slower (16 per lane)
+    // or needs more scalar registers than 8 waves per SIMD leave (8 per lane).
+    if (!(fabsf(acc[0]) <= 3.4028234663852886e38f)) {
+        if constexpr (OUT < 0) {
+            SrcCodes<EPL> d;
+            src_load(d, 0);
+            accumulate_direct<EPL, true>(acc, d);
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) acc[k] = 0.0f;
+        }
+        for (int i = OUT < 0 ? 1 : 0; i < K; ++i) {
+            SrcCodes<EPL> d;
+            src_load(d, i);
+            accumulate_direct<EPL, false>(acc, d);
+        }
+    }
+    finish_tile<BLOCK, EPL, OUT>(acc, e, out_codes, out_scales, out_vals, divisor, rdiv, thr,
+                                 slice);
 }
 
 // ---------------------------------------------------------------------------
