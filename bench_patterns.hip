@@ -7,7 +7,8 @@
 //    workgroups -- what plain streaming reaches on this GPU;
 //  * access patterns: for each libzpq kernel, the same per-lane loads and
 //    stores (widths, cache hints, lane layout, tiles per lane, sources in
-//    flight, grid shape, the slice reorder of the qgZ quantizer) with the
+//    flight, grid and workgroup shape, the slice reorder of the qgZ
+//    quantizer, the LDS-staged stores of averaged outputs) with the
 //    arithmetic replaced by XOR -- what the kernel's memory traffic alone
 //    costs.  Their outputs are meaningless;
 //  * VALU issue rates: one instruction kind (or one per-element instruction
@@ -191,7 +192,9 @@ __global__ __launch_bounds__(kThreads) void k_pat_receive(
     const uint8_t* __restrict__ in_codes, const uint32_t* __restrict__ in_scales, int32_t K,
     int64_t c, int32_t block, uint8_t* __restrict__ out_codes, uint32_t* __restrict__ out_scales,
     uint16_t* __restrict__ out_vals) {
-    const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * EPL;
+    constexpr int V = I4 ? 1 : EPL / 8;          // 16-byte output vectors per lane (float output)
+    __shared__ u32x4 stage[V >= 2 ? kThreads / 64 : 1][V >= 2 ? V * 64 : 1];
+    const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * EPL;
     if (e >= c) return;
     const int64_t cs = c / 2, ss = c / block;
     const uint32_t coff = (uint32_t)(e / 2), soff = (uint32_t)(e / block);
@@ -231,9 +234,28 @@ __global__ __launch_bounds__(kThreads) void k_pat_receive(
         const uint32_t lanes_per_block = (uint32_t)block / EPL;
         if ((threadIdx.x & (lanes_per_block - 1)) == 0) out_scales[e / block] = acc[0];
     } else {
-        u32x4* dst = reinterpret_cast<u32x4*>(out_vals + e);
+        u32x4 o[V];
 #pragma unroll
-        for (int k = 0; k < EPL / 8; ++k) stnt(u32x4{acc[k], acc[k] + 1, acc[k] + 2, acc[k] + 3}, dst + k);
+        for (int k = 0; k < V; ++k) o[k] = u32x4{acc[k], acc[k] + 1, acc[k] + 2, acc[k] + 3};
+        if (V >= 2 && __builtin_amdgcn_read_exec() == ~0ull) {
+            // A whole wave, as libzpq: lane-major into the wave's LDS slice, read
+            // back store-major, so that each store covers 1 KB contiguous.
+            const int lane = (int)(threadIdx.x & 63);
+            u32x4* slice = &stage[V >= 2 ? threadIdx.x / 64 : 0][0];
+#pragma unroll
+            for (int k = 0; k < V; ++k) slice[lane * V + k] = o[k];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = slice[k * 64 + lane];
+            __builtin_amdgcn_wave_barrier();
+            u32x4* dst = reinterpret_cast<u32x4*>(out_vals + (e - (int64_t)lane * EPL));
+#pragma unroll
+            for (int k = 0; k < V; ++k) stnt(o[k], dst + k * 64 + lane);
+        } else {
+            u32x4* dst = reinterpret_cast<u32x4*>(out_vals + e);
+#pragma unroll
+            for (int k = 0; k < V; ++k) stnt(o[k], dst + k);
+        }
     }
 }
 
@@ -430,7 +452,17 @@ int pat_reorder_quant_i4(const void* g, int64_t n, int32_t L, int32_t N, int32_t
 int pat_receive(const void* in_codes, const void* in_scales, int32_t K, int64_t c, int32_t block,
                 void* out_codes, void* out_scales, void* out_vals, int32_t epl, int32_t pf,
                 void* st) {
-    const unsigned g = grid_for(c, (int64_t)kThreads * epl);
+    // Workgroup size as libzpq's receive launch picks it: 4 waves, or 3 where
+    // that leaves fewer waves on the busiest compute unit.
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+        ncu = 256;
+    const int64_t waves = (c + 64LL * epl - 1) / (64LL * epl);
+    auto busiest = [&](int64_t w) { return ((waves + w - 1) / w + ncu - 1) / ncu * w; };
+    const unsigned nt = busiest(3) < busiest(4) ? 192u : 256u;
+    const unsigned g = grid_for(c, (int64_t)nt * epl);
     const hipStream_t s = (hipStream_t)st;
     const uint8_t* ic = (const uint8_t*)in_codes;
     const uint32_t* is = (const uint32_t*)in_scales;
@@ -438,13 +470,13 @@ int pat_receive(const void* in_codes, const void* in_scales, int32_t K, int64_t 
     uint32_t* os = (uint32_t*)out_scales;
     uint16_t* ov = (uint16_t*)out_vals;
     if (!out_vals && epl == 32 && pf == 2)
-        hipLaunchKernelGGL((k_pat_receive<32, 2, true>), dim3(g), dim3(kThreads), 0, s, ic, is, K,
+        hipLaunchKernelGGL((k_pat_receive<32, 2, true>), dim3(g), dim3(nt), 0, s, ic, is, K,
                            c, block, oc, os, ov);
     else if (out_vals && epl == 16 && pf == 2)
-        hipLaunchKernelGGL((k_pat_receive<16, 2, false>), dim3(g), dim3(kThreads), 0, s, ic, is, K,
+        hipLaunchKernelGGL((k_pat_receive<16, 2, false>), dim3(g), dim3(nt), 0, s, ic, is, K,
                            c, block, oc, os, ov);
     else if (out_vals && epl == 8 && pf == 4)
-        hipLaunchKernelGGL((k_pat_receive<8, 4, false>), dim3(g), dim3(kThreads), 0, s, ic, is, K,
+        hipLaunchKernelGGL((k_pat_receive<8, 4, false>), dim3(g), dim3(nt), 0, s, ic, is, K,
                            c, block, oc, os, ov);
     else
         return (int)hipErrorInvalidValue;
