@@ -634,7 +634,7 @@ def patterns(np, torch, zpq, synth, settle_s=0.1):
     P.pat_quant_i8.argtypes = [vp, i64, vp, vp, vp]
     P.pat_dequant_i8.argtypes = [vp, vp, i64, vp, vp]
     P.pat_reorder_quant_i4.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
-    P.pat_receive.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, vp]
+    P.pat_receive.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32, vp]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     T = torch
@@ -670,20 +670,33 @@ def patterns(np, torch, zpq, synth, settle_s=0.1):
         bufs = [e(n16 * 4, T.float32).fill_(1.0) for _ in range(n_sets(n16 * 16))]
         return n16 * 16, [(lambda b=b: ok(P.pat_read(ptr(b), n16 * 16, ptr(sink), S_))) for b in bufs]
 
-    def row(label, nbytes, make_k, make_p):
-        k_us, p_us = time_pair([make_k, make_p], nbytes)
+    def row(label, nbytes, make_k, make_p, parts=None):
+        """parts: for the receive kernels, make(i, parts) of the pattern with
+        only some of its accesses (bit 0 the scale loads, bit 1 the stores)."""
+        fams = [make_k, make_p]
+        if parts:
+            fams += [lambda i, b=b: parts(i, b) for b in (2, 1, 0)]
+        us = time_pair(fams, nbytes)
+        k_us, p_us = us[0], us[1]
         rb, fns = read_stream(nbytes)
         r_us = float(np.median(launch_groups_us(torch, fns, 10, settle_s)))
         del fns
-        rows.append({"kernel": label, "bytes": int(nbytes), "kernel_us": round(k_us, 2),
-                     "pattern_us": round(p_us, 2),
-                     "kernel_frac_of_peak": round(nbytes / k_us / 1e3 / HBM_PEAK_GBS, 4),
-                     "pattern_frac_of_peak": round(nbytes / p_us / 1e3 / HBM_PEAK_GBS, 4),
-                     "kernel_over_pattern": round(k_us / p_us, 3),
-                     "read_stream_bytes": rb, "read_stream_us": round(r_us, 2),
-                     "read_stream_frac_of_peak": round(rb / r_us / 1e3 / HBM_PEAK_GBS, 4)})
+        r = {"kernel": label, "bytes": int(nbytes), "kernel_us": round(k_us, 2),
+             "pattern_us": round(p_us, 2),
+             "kernel_frac_of_peak": round(nbytes / k_us / 1e3 / HBM_PEAK_GBS, 4),
+             "pattern_frac_of_peak": round(nbytes / p_us / 1e3 / HBM_PEAK_GBS, 4),
+             "kernel_over_pattern": round(k_us / p_us, 3),
+             "read_stream_bytes": rb, "read_stream_us": round(r_us, 2),
+             "read_stream_frac_of_peak": round(rb / r_us / 1e3 / HBM_PEAK_GBS, 4)}
+        if parts:
+            r.update({"pattern_without_scale_loads_us": round(us[2], 2),
+                      "pattern_without_stores_us": round(us[3], 2),
+                      "pattern_code_loads_only_us": round(us[4], 2)})
+        rows.append(r)
+        extra = (f"; without scale loads {us[2]:.2f}, without stores {us[3]:.2f}, code loads "
+                 f"only {us[4]:.2f}") if parts else ""
         print(f"[patterns] {label}: kernel {k_us:.2f} us, pattern {p_us:.2f} us, "
-              f"read stream of the same size {r_us:.2f} us", file=sys.stderr, flush=True)
+              f"read stream of the same size {r_us:.2f} us{extra}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
     cp = lambda t, i: t if i == 0 else t.clone()
@@ -749,13 +762,13 @@ def patterns(np, torch, zpq, synth, settle_s=0.1):
             o = (e(chunk // 2, T.uint8), e(chunk // B, T.float32))
             return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, L, chunk, B, out=o)
 
-        def h1_pattern(i):
+        def h1_pattern(i, parts=3):
             ci, si = cp(c1, i), cp(s1, i)
             o = (e(chunk // 2, T.uint8), e(chunk // B, T.float32))
             return lambda: ok(P.pat_receive(ptr(ci), ptr(si), L, chunk, B, ptr(o[0]), ptr(o[1]),
-                                            null, epl, pf, S_))
+                                            null, epl, pf, parts, S_))
         row(fl1_label, L * (chunk // 2 + chunk // B * 4) + chunk // 2 + chunk // B * 4,
-            h1_kernel, h1_pattern)
+            h1_kernel, h1_pattern, h1_pattern)
         if fl2_label:
             epl2, pf2 = receive_shape(S, N, True)
 
@@ -764,11 +777,11 @@ def patterns(np, torch, zpq, synth, settle_s=0.1):
                 return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, N, S, B, out_dtype=out_dt,
                                                                  divisor=float(W), out=yv)
 
-            def h2_pattern(i):
+            def h2_pattern(i, parts=3):
                 ci, si, yv = cp(c2, i), cp(s2, i), e(S, out_dt)
                 return lambda: ok(P.pat_receive(ptr(ci), ptr(si), N, S, B, null, null, ptr(yv),
-                                                epl2, pf2, S_))
-            row(fl2_label, N * (S // 2 + S // B * 4) + S * 2, h2_kernel, h2_pattern)
+                                                epl2, pf2, parts, S_))
+            row(fl2_label, N * (S // 2 + S // B * 4) + S * 2, h2_kernel, h2_pattern, h2_pattern)
 
     # c3: qgZ hop 1
     c = synth.QGZ_HOP1
@@ -789,12 +802,12 @@ def patterns(np, torch, zpq, synth, settle_s=0.1):
         return lambda: zpq.qgz_dequant_reduce_requant_i4(ci, si, K, chunk, B, out_dtype=T.bfloat16,
                                                          divisor=c["divisor"], out=yv)
 
-    def c4_pattern(i):
+    def c4_pattern(i, parts=3):
         ci, si, yv = cp(ic, i), cp(isc, i), e(chunk, T.bfloat16)
         return lambda: ok(P.pat_receive(ptr(ci), ptr(si), K, chunk, B, null, null, ptr(yv), epl, pf,
-                                        S_))
+                                        parts, S_))
     row("c4 K5 hop-2 16 x 2^24 -> bf16 average", K * (chunk // 2 + chunk // B * 4) + chunk * 2,
-        c4_kernel, c4_pattern)
+        c4_kernel, c4_pattern, c4_pattern)
     del ic, isc
     # c5: fused qgZ
     c = synth.QGZ_FUSED

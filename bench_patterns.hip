@@ -162,7 +162,7 @@ struct Src {
     uint32_t s;
 };
 
-template <int EPL>
+template <int EPL, bool SC>
 __device__ __forceinline__ void load(Src<EPL>& d, const uint8_t* c, uint32_t cb, uint32_t coff,
                                      const uint32_t* s, uint32_t sb, uint32_t soff) {
     const __amdgpu_buffer_rsrc_t rc = rsrc(c, cb);
@@ -178,7 +178,7 @@ __device__ __forceinline__ void load(Src<EPL>& d, const uint8_t* c, uint32_t cb,
             d.w[4 * i] = t[0]; d.w[4 * i + 1] = t[1]; d.w[4 * i + 2] = t[2]; d.w[4 * i + 3] = t[3];
         }
     }
-    d.s = __builtin_amdgcn_raw_buffer_load_b32(rsrc(s, sb), soff * 4, 0, 0);
+    d.s = SC ? __builtin_amdgcn_raw_buffer_load_b32(rsrc(s, sb), soff * 4, 0, 0) : soff;
 }
 
 template <int EPL>
@@ -187,7 +187,9 @@ __device__ __forceinline__ void mix(uint32_t (&acc)[EPL / 8], const Src<EPL>& d)
     for (int i = 0; i < EPL / 8; ++i) acc[i] ^= d.w[i] ^ d.s;
 }
 
-template <int EPL, int PF, bool I4>
+// SC: the per-source scale loads; ST: the output stores (both true for the
+// pattern proper; the others decompose its time).
+template <int EPL, int PF, bool I4, bool SC, bool ST>
 __global__ __launch_bounds__(kThreads) void k_pat_receive(
     const uint8_t* __restrict__ in_codes, const uint32_t* __restrict__ in_scales, int32_t K,
     int64_t c, int32_t block, uint8_t* __restrict__ out_codes, uint32_t* __restrict__ out_scales,
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void k_pat_receive(
     const uint32_t cb = (uint32_t)cs, sb = (uint32_t)(ss * 4);
     uint32_t acc[EPL / 8] = {};
     auto ld = [&](Src<EPL>& d, int i) {
-        load<EPL>(d, in_codes + (int64_t)i * cs, cb, coff, in_scales + (int64_t)i * ss, sb, soff);
+        load<EPL, SC>(d, in_codes + (int64_t)i * cs, cb, coff, in_scales + (int64_t)i * ss, sb, soff);
     };
     Src<EPL> buf[PF];
 #pragma unroll
@@ -220,6 +222,14 @@ __global__ __launch_bounds__(kThreads) void k_pat_receive(
         Src<EPL> d;
         ld(d, i);
         mix<EPL>(acc, d);
+    }
+    if constexpr (!ST) {
+        // Keeps the loads: the sum of every lane would have to hit one value.
+        if (acc[0] == 0x9E3779B9u && e == 0) {
+            if constexpr (I4) out_scales[0] = acc[0];
+            else out_vals[0] = 1;
+        }
+        return;
     }
     if constexpr (I4) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(out_codes + e / 2);
@@ -333,6 +343,7 @@ __global__ __launch_bounds__(kThreads) void k_valu_mul_f64(uint32_t* out, int it
         float a[8];                                                                        \
         uint32_t w[8];                                                                     \
         const float c = -8.0f * b;                                                         \
+        (void)c;                                                                           \
         for (int i = 0; i < 8; ++i) {                                                      \
             a[i] = 0.0f;                                                                    \
             w[i] = (threadIdx.x * 0x9E3779B9u + i) & 0x0F0F0F0Fu;                            \
@@ -396,6 +407,24 @@ inline unsigned grid_for(int64_t units, int64_t per_wg) {
     return (unsigned)((units + per_wg - 1) / per_wg);
 }
 
+template <int EPL, int PF, bool I4>
+int launch_pat_receive(unsigned g, unsigned nt, hipStream_t s, const uint8_t* ic,
+                       const uint32_t* is, int32_t K, int64_t c, int32_t block, uint8_t* oc,
+                       uint32_t* os, uint16_t* ov, int parts) {
+    switch (parts) {
+    case 3: hipLaunchKernelGGL((k_pat_receive<EPL, PF, I4, true, true>), dim3(g), dim3(nt), 0, s,
+                               ic, is, K, c, block, oc, os, ov); break;
+    case 2: hipLaunchKernelGGL((k_pat_receive<EPL, PF, I4, false, true>), dim3(g), dim3(nt), 0, s,
+                               ic, is, K, c, block, oc, os, ov); break;
+    case 1: hipLaunchKernelGGL((k_pat_receive<EPL, PF, I4, true, false>), dim3(g), dim3(nt), 0, s,
+                               ic, is, K, c, block, oc, os, ov); break;
+    case 0: hipLaunchKernelGGL((k_pat_receive<EPL, PF, I4, false, false>), dim3(g), dim3(nt), 0, s,
+                               ic, is, K, c, block, oc, os, ov); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -448,10 +477,11 @@ int pat_reorder_quant_i4(const void* g, int64_t n, int32_t L, int32_t N, int32_t
 }
 
 // K sources x c elements; I4 output (out_codes, out_scales) when out_vals is
-// NULL, else 16-bit values.  epl / pf: the launch shape libzpq picks.
+// NULL, else 16-bit values.  epl / pf: the launch shape libzpq picks.  parts:
+// bit 0 the scale loads, bit 1 the stores (3: the kernel's whole pattern).
 int pat_receive(const void* in_codes, const void* in_scales, int32_t K, int64_t c, int32_t block,
                 void* out_codes, void* out_scales, void* out_vals, int32_t epl, int32_t pf,
-                void* st) {
+                int32_t parts, void* st) {
     // Workgroup size as libzpq's receive launch picks it: 4 waves, or 3 where
     // that leaves fewer waves on the busiest compute unit.
     int dev = 0, ncu = 0;
@@ -470,17 +500,12 @@ int pat_receive(const void* in_codes, const void* in_scales, int32_t K, int64_t 
     uint32_t* os = (uint32_t*)out_scales;
     uint16_t* ov = (uint16_t*)out_vals;
     if (!out_vals && epl == 32 && pf == 2)
-        hipLaunchKernelGGL((k_pat_receive<32, 2, true>), dim3(g), dim3(nt), 0, s, ic, is, K,
-                           c, block, oc, os, ov);
-    else if (out_vals && epl == 16 && pf == 2)
-        hipLaunchKernelGGL((k_pat_receive<16, 2, false>), dim3(g), dim3(nt), 0, s, ic, is, K,
-                           c, block, oc, os, ov);
-    else if (out_vals && epl == 8 && pf == 4)
-        hipLaunchKernelGGL((k_pat_receive<8, 4, false>), dim3(g), dim3(nt), 0, s, ic, is, K,
-                           c, block, oc, os, ov);
-    else
-        return (int)hipErrorInvalidValue;
-    return hipGetLastError();
+        return launch_pat_receive<32, 2, true>(g, nt, s, ic, is, K, c, block, oc, os, ov, parts);
+    if (out_vals && epl == 16 && pf == 2)
+        return launch_pat_receive<16, 2, false>(g, nt, s, ic, is, K, c, block, oc, os, ov, parts);
+    if (out_vals && epl == 8 && pf == 4)
+        return launch_pat_receive<8, 4, false>(g, nt, s, ic, is, K, c, block, oc, os, ov, parts);
+    return (int)hipErrorInvalidValue;
 }
 
 // VALU issue-rate kernel `kind` (0 .. pat_valu_kinds() - 1) on `wgs`
