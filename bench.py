@@ -120,8 +120,10 @@ def parse():
                     help="measure the vector ALU's issue rate per instruction kind and per "
                          "per-element sequence of the hop-receive loop (register-only kernels "
                          "from bench_patterns.hip)")
-    ap.add_argument("--study", choices=["hop-count", "blocking"], default=None,
-                    help="run an error study instead of the throughput benchmark")
+    ap.add_argument("--study", choices=["hop-count", "blocking", "receive-shapes"], default=None,
+                    help="run a study instead of the throughput benchmark: hop-count and "
+                         "blocking (quantization error), receive-shapes (launch shapes of the "
+                         "receive kernel; needs the variant libraries)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 1 GiB with torch (a plain copy kernel of known "
                          "size, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -152,6 +154,9 @@ def main():
         return
     if args.study == "blocking":
         print(json.dumps(blocking_study(np, torch, zpq, synth)), flush=True)
+        return
+    if args.study == "receive-shapes":
+        print(json.dumps(receive_shapes_study(np, torch)), flush=True)
         return
     if args.per_config:
         print(json.dumps(per_config(np, torch, zpq, synth)), flush=True)
@@ -429,6 +434,156 @@ def verify(zpq, synth, np, torch, layer_h, grad_h, gath_codes, gath_scales, y_la
     pool.shutdown()
     return {"compared": "every output byte of every kernel of this run", "bit_exact": all(ok.values()),
             "parts": ok, "oracle_threads": workers, "seconds": round(time.time() - t0, 1)}
+
+
+# Build-time defaults of the receive launch (csrc/zpq.hip); the receive-shapes
+# study reads each variant's overrides against these to name the kernel a
+# launch uses.
+RECEIVE_DEFAULTS = {"ZPQ_REDUCE_EPL_I4": 32, "ZPQ_REDUCE_PF_I4": 2, "ZPQ_REDUCE_EPL_FL": 16,
+                    "ZPQ_REDUCE_PF_FL": 2, "ZPQ_REDUCE_PF_FL_NARROW": 4,
+                    "ZPQ_REDUCE_NARROW_WAVES": 8, "ZPQ_REDUCE_WG3": 0}
+
+
+def receive_launch(defines, K, c, B, fl, cus):
+    """(EPL, PF, threads per workgroup, mangled kernel-name fragment) of the
+    receive launch a library built with `defines` makes for K sources of c
+    elements, block B (fl: float output, 1 fp16 / 2 bf16; else INT4)."""
+    d = dict(RECEIVE_DEFAULTS)
+    for x in defines:
+        k, v = x[2:].split("=")
+        d[k] = int(v)
+
+    def epl_for(e):
+        return B if e > B else (e if B // e <= 32 else B // 32)
+    if not fl:
+        epl, pf, out = epl_for(d["ZPQ_REDUCE_EPL_I4"]), d["ZPQ_REDUCE_PF_I4"], "in1"
+    else:
+        waves16 = -(-c // (16 * 64))
+        if B <= 256 and waves16 < d["ZPQ_REDUCE_NARROW_WAVES"] * 4 * cus:
+            epl, pf = 8, d["ZPQ_REDUCE_PF_FL_NARROW"]
+        else:
+            epl, pf = epl_for(d["ZPQ_REDUCE_EPL_FL"]), d["ZPQ_REDUCE_PF_FL"]
+        out = f"i{fl}"
+    waves = -(-c // (64 * epl))
+    busiest = lambda w: -(-(-(-waves // w)) // cus) * w
+    nt = 192 if d["ZPQ_REDUCE_WG3"] and busiest(3) < busiest(4) else 256
+    return epl, pf, nt, f"k_dequant_reduceILi{B}ELi{epl}EL{out}ELi{pf}E"
+
+
+def receive_shapes_study(np, torch, settle_s=0.1):
+    """The receive kernel's launch shapes side by side: every library of
+    block_quantized_communication_amd/variants/ (built by
+    `python -m block_quantized_communication_amd.build --variants`, one
+    build-time override each: elements per lane, sources in flight, when the
+    average takes 8 per lane, 3-wave workgroups) on the four receive
+    workloads, alternating with the default build, each output compared
+    byte for byte with the default's, with the registers, LDS and occupancy
+    the compiler reported for the kernel the launch uses.  Then the default
+    hop-1 kernel at 1..16 sources (block 128),
+    whose VALU instructions per wave (a counter pass over this command) give
+    the per-source loop and the fixed part of each tile, the epilogue (the
+    chunk is 2^25 + 8192 K elements, so that each K has a grid of its own)."""
+    import ctypes
+    vdir = os.path.join(ROOT, "block_quantized_communication_amd", "variants")
+    rpath = os.path.join(vdir, "resources.json")
+    if not os.path.exists(rpath):
+        raise RuntimeError("no receive variants: run python -m "
+                           "block_quantized_communication_amd.build --variants")
+    with open(rpath) as f:
+        report = json.load(f)
+    names = [n for n in report if os.path.exists(os.path.join(vdir, f"libzpq_{n}.so"))]
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    libs = {}
+    for n in names:
+        lib = ctypes.CDLL(os.path.join(vdir, f"libzpq_{n}.so"))
+        lib.zpq_qgz_dequant_reduce_requant_i4.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32,
+                                                          f32, vp]
+        libs[n] = lib
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    # (label, sources, chunk, block, float output: 0 INT4 / 1 fp16 / 2 bf16, divisor)
+    W = [("c3 hop 1: 8 x 2^25 -> INT4, B=128", 8, 1 << 25, 128, 0, 1.0),
+         ("c4 hop 2: 16 x 2^24 -> bf16 average, B=128", 16, 1 << 24, 128, 2, 16.0),
+         ("c5 hop 1: 8 x 132M -> INT4, B=64", 8, 132120576, 64, 0, 1.0),
+         ("c5 hop 2: 48 x 2.75M -> fp16 average, B=64", 48, 2752512, 64, 1, 384.0)]
+
+    def buffers(K, c, B, fl):
+        nbytes = K * (c // 2 + c // B * 4) + (c * 2 if fl else c // 2 + c // B * 4)
+        sets = []
+        for _ in range(n_sets(nbytes)):
+            codes = torch.randint(0, 256, (K * c // 2,), dtype=torch.uint8, device=dev, generator=gen)
+            scales = torch.rand(K * c // B, device=dev, generator=gen) * 1e-3 + 1e-6
+            out = ((torch.empty(c, dtype=torch.int16, device=dev),) if fl else
+                   (torch.empty(c // 2, dtype=torch.uint8, device=dev),
+                    torch.empty(c // B, dtype=torch.float32, device=dev)))
+            sets.append((codes, scales, out))
+        return nbytes, sets
+
+    def caller(lib, s, K, c, B, fl, div):
+        codes, scales, out = s
+        if fl:
+            a = (codes.data_ptr(), scales.data_ptr(), K, c, B, None, None, out[0].data_ptr(), fl,
+                 div, st)
+        else:
+            a = (codes.data_ptr(), scales.data_ptr(), K, c, B, out[0].data_ptr(),
+                 out[1].data_ptr(), None, 0, 1.0, st)
+        f = lib.zpq_qgz_dequant_reduce_requant_i4
+
+        def run():
+            rc = f(*a)
+            if rc != 0:
+                raise RuntimeError(f"receive launch failed ({rc})")
+        return run
+
+    rows = []
+    for label, K, c, B, fl, div in W:
+        nbytes, sets = buffers(K, c, B, fl)
+        ref = None
+        outs = {}
+        for n in names:
+            caller(libs[n], sets[0], K, c, B, fl, div)()
+            torch.cuda.synchronize()
+            outs[n] = [t.clone() for t in sets[0][2]]
+        times = {n: [] for n in names}
+        for rep in range(2):                       # all libraries in turn, then in reverse
+            for n in (names if rep == 0 else names[::-1]):
+                times[n] += launch_groups_us(torch, [caller(libs[n], x, K, c, B, fl, div)
+                                                     for x in sets], 5, settle_s)
+        ref = outs["default"]
+        for n in names:
+            epl, pf, nt, frag = receive_launch(report[n]["defines"], K, c, B, fl, cus)
+            res = next((r for k, r in report[n]["kernels"].items() if frag in k), {})
+            us = float(np.median(times[n]))
+            rows.append({"workload": label, "variant": n, "defines": report[n]["defines"],
+                         "elements_per_lane": epl, "sources_in_flight": pf,
+                         "threads_per_workgroup": nt, "kernel_resources": res,
+                         "us": round(us, 2), "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "identical_to_default": all(torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+                                                     for a, b in zip(outs[n], ref))})
+            print(f"[receive-shapes] {label} {n}: {us:.2f} us (EPL {epl}, {pf} in flight, "
+                  f"{nt} threads, {res.get('vgprs')} VGPRs, {res.get('waves_per_simd')} waves/SIMD)",
+                  file=sys.stderr, flush=True)
+        del sets, outs
+        torch.cuda.empty_cache()
+    ksweep = []
+    for K in (1, 2, 4, 8, 16):
+        c, B = (1 << 25) + 8192 * K, 128            # a grid of its own per K, for the counters
+        nbytes, sets = buffers(K, c, B, 0)
+        us = float(np.median(launch_groups_us(torch, [caller(libs["default"], x, K, c, B, 0, 1.0)
+                                                      for x in sets], 10, settle_s)))
+        ksweep.append({"sources": K, "chunk": c, "block": B, "bytes": nbytes, "us": round(us, 2),
+                       "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        print(f"[receive-shapes] hop 1 K={K}: {us:.2f} us", file=sys.stderr, flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    return {"study": "receive-shapes", "rows": rows, "hop1_source_sweep": ksweep,
+            "timing": f"per-launch time of {LAUNCHES} back-to-back launches between one HIP event "
+                      "pair, buffer sets rotated; the libraries alternate in runs of 5 groups, twice; "
+                      "median of the 10 groups", "peak_GBps": HBM_PEAK_GBS}
 
 
 def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):

@@ -1,6 +1,12 @@
 """Build libzpq.so (HIP, gfx950) in-tree, next to this file.
 
   python -m block_quantized_communication_amd.build [-v] [--save-temps]
+  python -m block_quantized_communication_amd.build --variants
+
+--variants builds the receive-kernel launch-shape variants that
+bench.py --study receive-shapes compares (RECEIVE_VARIANTS: one build-time
+override each) into variants/, with the compiler's register, LDS and
+occupancy report for every receive kernel in variants/resources.json.
 
 Flags: -O3 for gfx950 only; packed-FP32 instructions disabled; no fast-math
 (IEEE division, denormals kept); -fPIC shared library with a C ABI.
@@ -43,5 +49,87 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     return LIB
 
 
+# Launch-shape variants of the receive kernels (k_dequant_reduce): name ->
+# build-time overrides of the defaults in csrc/zpq.hip.
+RECEIVE_VARIANTS = {
+    "default": [],
+    "i4_pf1": ["-DZPQ_REDUCE_PF_I4=1"],
+    "i4_pf4": ["-DZPQ_REDUCE_PF_I4=4"],
+    "i4_epl16": ["-DZPQ_REDUCE_EPL_I4=16"],
+    "i4_epl16_pf4": ["-DZPQ_REDUCE_EPL_I4=16", "-DZPQ_REDUCE_PF_I4=4"],
+    "fl_narrow_pf2": ["-DZPQ_REDUCE_PF_FL_NARROW=2"],
+    "fl_narrow_pf8": ["-DZPQ_REDUCE_PF_FL_NARROW=8"],
+    "fl_wide_pf4": ["-DZPQ_REDUCE_PF_FL=4"],
+    "fl_never_narrow": ["-DZPQ_REDUCE_NARROW_WAVES=0"],
+    "fl_always_narrow": ["-DZPQ_REDUCE_NARROW_WAVES=1048576"],
+    "wg3": ["-DZPQ_REDUCE_WG3=1"],
+}
+VARIANTS_DIR = os.path.join(HERE, "variants")
+
+
+def _resources(stderr):
+    """Per-kernel register, LDS and occupancy report from the compiler's
+    kernel-resource-usage remarks: {mangled name: {field: int}}."""
+    import re
+    out, cur = {}, None
+    fields = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs",
+              "ScratchSize [bytes/lane]": "scratch_bytes_per_lane",
+              "Occupancy [waves/SIMD]": "waves_per_simd", "LDS Size [bytes/block]": "lds_bytes"}
+    for line in stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1) if "k_dequant_reduce" in m.group(1) else None
+            if cur:
+                out[cur] = {}
+            continue
+        if cur:
+            m = re.search(r"remark:\s+([^:]+(?:\[[^]]*\])?): (\d+)", line)
+            if m and m.group(1).strip() in fields:
+                out[cur][fields[m.group(1).strip()]] = int(m.group(2))
+    return out
+
+
+def build_variants(names=None, jobs=8, verbose=False):
+    """Build the RECEIVE_VARIANTS libraries (all, or `names`) into
+    variants/libzpq_<name>.so, `jobs` compilers at a time; write the
+    compiler's resource report of each variant's receive kernels to
+    variants/resources.json.  Returns the paths."""
+    import concurrent.futures
+    import json
+    os.makedirs(VARIANTS_DIR, exist_ok=True)
+    names = list(RECEIVE_VARIANTS) if names is None else list(names)
+
+    def one(name):
+        out = os.path.join(VARIANTS_DIR, f"libzpq_{name}.so")
+        cmd = ["hipcc", *HIPCC_FLAGS, *RECEIVE_VARIANTS[name], "-Rpass-analysis=kernel-resource-usage",
+               f"-I{INCLUDE}", SRC, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for variant {name} ({res.returncode}):\n{res.stderr[-4000:]}")
+        os.replace(out + ".tmp", out)
+        return name, out, _resources(res.stderr)
+
+    report, paths = {}, []
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        for name, out, res in ex.map(one, names):
+            report[name] = {"defines": RECEIVE_VARIANTS[name], "kernels": res}
+            paths.append(out)
+    rpath = os.path.join(VARIANTS_DIR, "resources.json")
+    old = {}
+    if os.path.exists(rpath):
+        with open(rpath) as f:
+            old = json.load(f)
+    old.update(report)
+    with open(rpath, "w") as f:
+        json.dump(old, f, indent=1)
+    return paths
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv, save_temps="--save-temps" in sys.argv)
+    if "--variants" in sys.argv:
+        for p in build_variants(verbose="-v" in sys.argv):
+            print(p)
+    else:
+        build(verbose="-v" in sys.argv, save_temps="--save-temps" in sys.argv)

@@ -83,6 +83,9 @@
 #ifndef ZPQ_REDUCE_NARROW_WAVES
 #define ZPQ_REDUCE_NARROW_WAVES 8  // hop 2: 8 elements per lane below this many waves per SIMD
 #endif
+#ifndef ZPQ_REDUCE_WG3
+#define ZPQ_REDUCE_WG3 0           // receive: 3-wave workgroups where they spread waves more evenly
+#endif
 // Persistent grids: workgroups per compute unit (0 = one workgroup per
 // virtual block, no loop).
 #ifndef ZPQ_PERSIST_QUANT
@@ -1258,14 +1261,16 @@ constexpr int epl_for() {
 }
 
 // Threads per workgroup of a receive launch over c elements at EPL per lane:
-// kThreads (4 waves), or one wave fewer where that leaves fewer waves on the
-// busiest compute unit (the dispatcher spreads workgroups evenly over the
-// CUs).  For example, the 48-source hop 2 of a 138B-model layer has 5376
-// waves: 1344 workgroups of 4 put 24 waves on 64 of the 256 CUs and 20 on the
-// rest, and 1792 of 3 put 21 on every CU (measured: 7% faster).
+// kThreads (4 waves), or, built with ZPQ_REDUCE_WG3, one wave fewer where
+// that leaves fewer waves on the busiest compute unit (the dispatcher spreads
+// workgroups evenly over the CUs).  For example, the 48-source hop 2 of a
+// 138B-model layer has 5376 waves: 1344 workgroups of 4 put 24 waves on 64 of
+// the 256 CUs and 20 on the rest, 1792 of 3 put 21 on every CU.  Measured
+// against 4-wave workgroups: faster on two boards, 4-7% slower on four, so
+// it is off by default.
 inline unsigned reduce_threads(int64_t c, int epl) {
     constexpr int64_t wmax = kThreads / 64;
-    if (wmax < 2) return kThreads;
+    if (wmax < 2 || !ZPQ_REDUCE_WG3) return kThreads;
     const int64_t waves = (c + 64LL * epl - 1) / (64LL * epl);
     const int64_t n = cu_count();
     auto busiest = [&](int64_t w) { return ((waves + w - 1) / w + n - 1) / n * w; };

@@ -188,3 +188,25 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         zpq.qgz_dequant_reduce_requant_i4(torch.zeros(1024, dtype=torch.uint8),
                                            torch.zeros(16), 2, 1024, 128)
+
+
+def test_receive_launch_names_the_shapes_libzpq_picks():
+    """bench.py's receive-shapes study names the kernel each launch uses; on
+    256 CUs the fused workload's 48-source average takes 8 elements per lane
+    and 4 sources in flight (3-wave workgroups when built with them), the
+    hop 1 of 8 x 2^25 takes 32 per lane and 2 in flight, and overrides
+    apply."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.receive_launch([], 48, 2752512, 64, 1, 256) == (
+        8, 4, 256, "k_dequant_reduceILi64ELi8ELi1ELi4E")
+    assert bench.receive_launch(["-DZPQ_REDUCE_WG3=1"], 48, 2752512, 64, 1, 256)[2] == 192
+    assert bench.receive_launch(["-DZPQ_REDUCE_WG3=1"], 8, 1 << 25, 128, 0, 256)[2] == 256
+    assert bench.receive_launch([], 8, 1 << 25, 128, 0, 256) == (
+        32, 2, 256, "k_dequant_reduceILi128ELi32ELin1ELi2E")
+    assert bench.receive_launch([], 16, 1 << 24, 128, 2, 256) == (
+        16, 2, 256, "k_dequant_reduceILi128ELi16ELi2ELi2E")
+    assert bench.receive_launch(["-DZPQ_REDUCE_NARROW_WAVES=0"], 48, 2752512, 64, 1, 256)[:2] == (16, 2)
+    assert bench.receive_launch(["-DZPQ_REDUCE_EPL_I4=16", "-DZPQ_REDUCE_PF_I4=4"],
+                                8, 1 << 25, 128, 0, 256)[:2] == (16, 4)

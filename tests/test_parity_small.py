@@ -260,18 +260,16 @@ def test_requant_near_ties():
 
 @pytest.mark.parametrize("waves", [1023, 1025])
 @pytest.mark.parametrize("mode", ["i4", "f16"])
-def test_dequant_reduce_workgroup_shapes(mode, waves):
-    """Receive launches in both workgroup shapes.  The launch uses 4-wave
-    workgroups unless 3-wave ones leave fewer waves on the busiest compute
-    unit; on 256 CUs a launch of 1023 waves takes 4-wave workgroups and one of
-    1025 takes 3-wave ones.  The last wave is partly empty (a ragged tail of
-    3 blocks)."""
+def test_dequant_reduce_ragged_last_wave(mode, waves):
+    """Receive launches of 1023 and 1025 waves (a last workgroup with 3 of
+    its 4 waves busy, and one with 1) whose last wave is partly empty: a
+    ragged tail of 3 blocks."""
     rng = np.random.default_rng(waves)
     K = 5
     block, epl = (128, 32) if mode == "i4" else (64, 8)      # the launch's elements per lane
     chunk = (waves - 1) * 64 * epl + 3 * block
     codes, s = random_received(rng, K, chunk, block)
-    print(f"dequant_reduce workgroup shapes mode={mode} waves={waves} chunk={chunk}",
+    print(f"dequant_reduce ragged last wave mode={mode} waves={waves} chunk={chunk}",
           flush=True)
     if mode == "i4":
         oc, os_ = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk,
