@@ -188,18 +188,22 @@ def test_dequant_reduce_average_overflowing_sums(out, divisor):
 
 @pytest.mark.parametrize("out", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("tail", [0, 128 * 3])
-def test_dequant_reduce_average_long_chunk(out, tail):
+@pytest.mark.parametrize("divisor", [3.0, 16.0, 2.0 ** 127, 2.0 ** -126])
+def test_dequant_reduce_average_long_chunk(out, tail, divisor):
     """A chunk long enough for the hop-2 launch with 16 elements per lane
     (short chunks take 8 per lane): 2^23 + 2^16 elements, 3 sources; with a
     tail, the last wave is partly empty and writes its outputs lane by lane
-    (whole waves write theirs as coalesced 1 KB stores)."""
+    (whole waves write theirs as coalesced 1 KB stores).  Powers of two take
+    the multiply by 2^-k at this width: 2^127 makes subnormal and zero
+    averages, 2^-126 overflowing ones."""
     rng = np.random.default_rng(77 + tail)
     K, block, chunk = 3, 128, (1 << 23) + (1 << 16) + tail
     codes, s = random_received(rng, K, chunk, block)
-    print(f"dequant_reduce_average long chunk out={out} K={K} chunk={chunk} tail={tail}", flush=True)
+    print(f"dequant_reduce_average long chunk out={out} K={K} chunk={chunk} tail={tail} "
+          f"div={divisor}", flush=True)
     y = zpq.qgz_dequant_reduce_requant_i4(to_device(codes), to_device(s), K, chunk, block,
-                                           out_dtype=torch_dt(out), divisor=3.0)
-    ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, out, 3.0)
+                                           out_dtype=torch_dt(out), divisor=divisor)
+    ref = oracle.qgz_dequant_reduce_requant_i4(codes, s, K, chunk, block, out, divisor)
     assert_bits_equal(from_device(y), ref, "values")
 
 
