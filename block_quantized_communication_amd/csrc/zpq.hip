@@ -952,7 +952,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
     constexpr int V = OutVectors<OUT, EPL>::v;
     __shared__ u32x4 stage[V >= 2 ? kThreads / 64 : 1][V >= 2 ? V * 64 : 1];
     u32x4* const slice = &stage[V >= 2 ? threadIdx.x / 64 : 0][0];
-    // kThreads or kThreads - 64 threads per workgroup (the launch picks).
+    // kThreads threads per workgroup, or kThreads - 64 where a build with
+    // ZPQ_REDUCE_WG3 picks 3-wave workgroups (reduce_threads).
     for (uint32_t k = blockIdx.x; k < nvb; k += gridDim.x) {
     const uint32_t vb = tile_of<ZPQ_XCD_REDUCE>(k, nvb);
         const int64_t e = ((int64_t)vb * blockDim.x + threadIdx.x) * EPL;
