@@ -60,6 +60,8 @@ RECEIVE_VARIANTS = {
     "fl_narrow_pf2": ["-DZPQ_REDUCE_PF_FL_NARROW=2"],
     "fl_narrow_pf8": ["-DZPQ_REDUCE_PF_FL_NARROW=8"],
     "fl_wide_pf4": ["-DZPQ_REDUCE_PF_FL=4"],
+    "fl_wide_epl32": ["-DZPQ_REDUCE_EPL_FL=32"],
+    "fl_wide_xcd": ["-DZPQ_XCD_REDUCE=1"],
     "fl_never_narrow": ["-DZPQ_REDUCE_NARROW_WAVES=0"],
     "fl_always_narrow": ["-DZPQ_REDUCE_NARROW_WAVES=1048576"],
     "wg3": ["-DZPQ_REDUCE_WG3=1"],
