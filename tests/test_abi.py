@@ -210,3 +210,26 @@ def test_receive_launch_names_the_shapes_libzpq_picks():
     assert bench.receive_launch(["-DZPQ_REDUCE_NARROW_WAVES=0"], 48, 2752512, 64, 1, 256)[:2] == (16, 2)
     assert bench.receive_launch(["-DZPQ_REDUCE_EPL_I4=16", "-DZPQ_REDUCE_PF_I4=4"],
                                 8, 1 << 25, 128, 0, 256)[:2] == (16, 4)
+
+
+def test_variant_build_reads_the_compiler_resource_report():
+    """build --variants keeps the compiler's register and occupancy report of
+    every receive kernel (kernel-resource-usage remarks), and only those."""
+    from block_quantized_communication_amd import build as hip_build
+    text = "\n".join([
+        "zpq.hip:938:1: remark: Function Name: _ZN12_GLOBAL__N_116k_dequant_reduceILi64ELi32ELin1ELi2EEEvPKhPKf [-Rpass-analysis=kernel-resource-usage]",
+        "zpq.hip:938:1: remark:     TotalSGPRs: 92 [-Rpass-analysis=kernel-resource-usage]",
+        "zpq.hip:938:1: remark:     VGPRs: 64 [-Rpass-analysis=kernel-resource-usage]",
+        "zpq.hip:938:1: remark:     AGPRs: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "zpq.hip:938:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "zpq.hip:938:1: remark:     Occupancy [waves/SIMD]: 8 [-Rpass-analysis=kernel-resource-usage]",
+        "zpq.hip:938:1: remark:     LDS Size [bytes/block]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "zpq.hip:436:1: remark: Function Name: _ZN12_GLOBAL__N_110k_quant_i8ILi1ELi256ELi8ELi2EEEvPKvlPaPfj [-Rpass-analysis=kernel-resource-usage]",
+        "zpq.hip:436:1: remark:     VGPRs: 38 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    r = hip_build._resources(text)
+    assert list(r) == ["_ZN12_GLOBAL__N_116k_dequant_reduceILi64ELi32ELin1ELi2EEEvPKhPKf"]
+    assert r[next(iter(r))] == {"sgprs": 92, "vgprs": 64, "agprs": 0, "scratch_bytes_per_lane": 0,
+                                "waves_per_simd": 8, "lds_bytes": 0}
+    assert all(v for v in hip_build.RECEIVE_VARIANTS.values() if v) and \
+        hip_build.RECEIVE_VARIANTS["default"] == []
