@@ -69,9 +69,10 @@ RECEIVE_VARIANTS = {
 VARIANTS_DIR = os.path.join(HERE, "variants")
 
 
-def _resources(stderr):
+def _resources(stderr, only="k_dequant_reduce"):
     """Per-kernel register, LDS and occupancy report from the compiler's
-    kernel-resource-usage remarks: {mangled name: {field: int}}."""
+    kernel-resource-usage remarks: {mangled name: {field: int}}, for the
+    kernels whose name contains `only` (all of them for "")."""
     import re
     out, cur = {}, None
     fields = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs",
@@ -80,7 +81,7 @@ def _resources(stderr):
     for line in stderr.splitlines():
         m = re.search(r"remark: Function Name: (\S+)", line)
         if m:
-            cur = m.group(1) if "k_dequant_reduce" in m.group(1) else None
+            cur = m.group(1) if only in m.group(1) else None
             if cur:
                 out[cur] = {}
             continue
