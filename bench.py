@@ -138,7 +138,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: libzpq has no multi-GPU path "
               "(collectives are simulated in one GPU's memory); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
