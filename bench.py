@@ -492,6 +492,9 @@ def receive_shapes_study(np, torch, settle_s=0.1):
     with open(rpath) as f:
         report = json.load(f)
     names = [n for n in report if os.path.exists(os.path.join(vdir, f"libzpq_{n}.so"))]
+    if "default" not in names:
+        raise RuntimeError("the default variant library is missing: run python -m "
+                           "block_quantized_communication_amd.build --variants")
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     libs = {}
     for n in names:
