@@ -36,6 +36,12 @@ __device__ __forceinline__ void stnt(T v, T* p) { __builtin_nontemporal_store(v,
 
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
+// Raw-buffer descriptor over `bytes` bytes from a wave-uniform `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
 // ---------------------------------------------------------------------------
 // Ceilings.  n16 = number of 16-byte units; tile = 256 lanes x 16 bytes.
 __global__ __launch_bounds__(kThreads) void k_read(const u32x4* __restrict__ src, int64_t n16,
@@ -117,8 +123,9 @@ __global__ __launch_bounds__(kThreads) void k_pat_dequant_i8(const u32x2* __rest
 
 // qgZ reorder + INT4 quantize (fp16/bf16 in, block 64 or 128): slice-major
 // workgroups (send position p = j*N + m reads slice m*L + j), two tiles per
-// lane, one 16-byte load and one 4-byte code store per lane and tile, one
-// scale store per block.
+// lane, one 16-byte load and one 4-byte code store per lane and tile (a
+// buffer store with cache policy sc0 sc1 nt through a descriptor based at the
+// workgroup's codes, as libzpq), one scale store per block.
 __global__ __launch_bounds__(kThreads) void k_pat_reorder_quant_i4(
     const u32x4* __restrict__ g, int64_t S, int32_t L, int32_t N, uint32_t wgs_per_slice,
     int32_t block, uint32_t* __restrict__ codes, uint32_t* __restrict__ scales) {
@@ -128,6 +135,7 @@ __global__ __launch_bounds__(kThreads) void k_pat_reorder_quant_i4(
     const int64_t src0 = ((int64_t)m * L + j) * S, dst0 = (int64_t)p * S;
     const int64_t f0 = (int64_t)w * (2 * kThreads * 8);
     const uint32_t lanes_per_block = (uint32_t)block / 8;
+    const __amdgpu_buffer_rsrc_t rc = rsrc(codes + (dst0 + f0) / 8, 2 * kThreads * 8 / 2);
     u32x4 v[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void k_pat_reorder_quant_i4(
         const int64_t f = f0 + u * (kThreads * 8) + threadIdx.x * 8;
         if (f < S) {
             const int64_t e = dst0 + f;
-            stnt(fold(v[u]), codes + e / 8);
+            __builtin_amdgcn_raw_buffer_store_b32(fold(v[u]), rc, (uint32_t)(f - f0) / 2, 0, 19);
             if ((threadIdx.x & (lanes_per_block - 1)) == 0) scales[e / block] = v[u].x;
         }
     }
@@ -151,10 +159,6 @@ __global__ __launch_bounds__(kThreads) void k_pat_reorder_quant_i4(
 // scale per block (INT4 output) or EPL 16-bit values (float output).
 constexpr int kAux = 2;        // non-temporal loads
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
 template <int EPL>
 struct Src {

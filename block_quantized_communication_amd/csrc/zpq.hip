@@ -136,6 +136,12 @@
 #ifndef ZPQ_NTS_QGZ
 #define ZPQ_NTS_QGZ 1
 #endif
+// Cache-policy bits of the qgZ quantizer's code stores, issued as buffer
+// stores through a descriptor based at the workgroup's codes (19: sc0 sc1 nt);
+// -1: global stores with the ZPQ_NTS_QGZ hint instead.
+#ifndef ZPQ_CPOL_QGZ
+#define ZPQ_CPOL_QGZ 19
+#endif
 #ifndef ZPQ_NTL_REDUCE
 #define ZPQ_NTL_REDUCE 1
 #endif
@@ -158,6 +164,25 @@ template <bool NT, class T>
 __device__ __forceinline__ void st_stream(T v, T* p) {
     if constexpr (NT) __builtin_nontemporal_store(v, p);
     else *p = v;
+}
+
+// Buffer descriptor over `bytes` bytes from the wave-uniform address `base`
+// (held in SGPRs); lanes supply 32-bit byte offsets, and an access past
+// `bytes` reads zeros or is dropped instead of faulting.  Word 3 0x00020000
+// is the raw-buffer format for the gfx9 family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// A store through a descriptor at byte offset `off`, with the cache-policy
+// bits CPOL (bit 0 sc0, bit 1 nt, bit 4 sc1).
+template <int CPOL, class T>
+__device__ __forceinline__ void st_desc(T v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8 || sizeof(T) == 16, "4, 8 or 16 bytes");
+    if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CPOL);
+    else if constexpr (sizeof(T) == 8) __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, CPOL);
+    else __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, CPOL);
 }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -364,6 +389,23 @@ __device__ __forceinline__ void store_nibbles(uint8_t* dst, const uint32_t* pack
             st_stream<NT>(u32x4{packed[4 * k], packed[4 * k + 1], packed[4 * k + 2],
                                 packed[4 * k + 3]},
                           reinterpret_cast<u32x4*>(dst) + k);
+    }
+}
+
+// The same through a descriptor, from byte offset `off`, cache-policy bits CPOL.
+template <int EPL, int CPOL>
+__device__ __forceinline__ void store_nibbles(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                              const uint32_t* packed) {
+    if constexpr (EPL == 8) {
+        st_desc<CPOL>(packed[0], r, off);
+    } else if constexpr (EPL == 16) {
+        st_desc<CPOL>(u32x2{packed[0], packed[1]}, r, off);
+    } else {
+        static_assert(EPL % 32 == 0, "16-byte stores");
+#pragma unroll
+        for (int k = 0; k < EPL / 32; ++k)
+            st_desc<CPOL>(u32x4{packed[4 * k], packed[4 * k + 1], packed[4 * k + 2],
+                                packed[4 * k + 3]}, r, off + 16 * k);
     }
 }
 
@@ -714,6 +756,12 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
     const int64_t src0 = ((int64_t)m * L + j) * S;      // first element of slice m*L + j
     const int64_t dst0 = (int64_t)p * S;                 // first element of send position p
     const int64_t f0 = (int64_t)w * (U * kThreads * EPL);
+    // The workgroup's codes (U * kThreads * EPL / 2 contiguous bytes) go out
+    // as buffer stores with cache policy sc0 sc1 nt: measured 2-3% faster
+    // than non-temporal global stores on the 2^28 and 1.06G workloads (sc1
+    // alone, or nt alone, equal or slower once the outputs rotate so that
+    // none stays in the last-level cache).
+    const __amdgpu_buffer_rsrc_t rc = rsrc(codes + (dst0 + f0) / 2, U * kThreads * EPL / 2);
     InTile<DT, EPL> tile[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -739,7 +787,10 @@ __global__ __launch_bounds__(kThreads) void k_reorder_quant_i4(
             uint32_t packed[EPL / 8];
 #pragma unroll
             for (int k = 0; k < EPL / 8; ++k) packed[k] = pack_nibbles(q + 8 * k);
-            store_nibbles<EPL, ZPQ_NTS_QGZ>(codes + e / 2, packed);
+            if constexpr (ZPQ_CPOL_QGZ >= 0)
+                store_nibbles<EPL, ZPQ_CPOL_QGZ>(rc, (uint32_t)(f - f0) / 2, packed);
+            else
+                store_nibbles<EPL, ZPQ_NTS_QGZ>(codes + e / 2, packed);
             if ((threadIdx.x & (G - 1)) == 0) scales[e / BLOCK] = bs.s;
         }
     }
@@ -776,19 +827,13 @@ struct SrcCodes {
     float s;
 };
 
-// Received sources are read through buffer descriptors: the source's base
-// address lives in SGPRs (advanced per source by scalar adds) and each lane
-// supplies only a 32-bit byte offset, so the source loop spends no vector
-// instructions on addresses.  A descriptor covers exactly one source's chunk
-// (codes) or scale vector; an offset past it would read zeros, not fault.
-// Word 3 0x00020000 is the raw-buffer format for the gfx9 family.
+// Received sources are read through buffer descriptors (rsrc): the source's
+// base address lives in SGPRs (advanced per source by scalar adds) and each
+// lane supplies only a 32-bit byte offset, so the source loop spends no
+// vector instructions on addresses.  A descriptor covers exactly one source's
+// chunk (codes) or scale vector; an offset past it would read zeros, not fault.
 // Cache-policy operand of the code loads: 2 is the non-temporal bit.
 constexpr int kAuxReduce = ZPQ_NTL_REDUCE ? 2 : 0;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 
 template <int EPL>
 __device__ __forceinline__ void load_src(SrcCodes<EPL>& d, const uint8_t* cbase, uint32_t cbytes,
