@@ -120,10 +120,13 @@ def parse():
                     help="measure the vector ALU's issue rate per instruction kind and per "
                          "per-element sequence of the hop-receive loop (register-only kernels "
                          "from bench_patterns.hip)")
-    ap.add_argument("--study", choices=["hop-count", "blocking", "receive-shapes"], default=None,
+    ap.add_argument("--study", choices=["hop-count", "blocking", "receive-shapes", "store-policy"],
+                    default=None,
                     help="run a study instead of the throughput benchmark: hop-count and "
                          "blocking (quantization error), receive-shapes (launch shapes of the "
-                         "receive kernel; needs the variant libraries)")
+                         "receive kernel; needs the variant libraries), store-policy (cache-policy "
+                         "bits of streams and of the qgZ quantizer's code stores; needs the "
+                         "variant libraries)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 1 GiB with torch (a plain copy kernel of known "
                          "size, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -157,6 +160,8 @@ def main():
         return
     if args.study == "receive-shapes":
         print(json.dumps(receive_shapes_study(np, torch)), flush=True)
+    if args.study == "store-policy":
+        print(json.dumps(store_policy_study(np, torch)), flush=True)
         return
     if args.per_config:
         print(json.dumps(per_config(np, torch, zpq, synth)), flush=True)
@@ -491,7 +496,8 @@ def receive_shapes_study(np, torch, settle_s=0.1):
                            "block_quantized_communication_amd.build --variants")
     with open(rpath) as f:
         report = json.load(f)
-    names = [n for n in report if os.path.exists(os.path.join(vdir, f"libzpq_{n}.so"))]
+    names = [n for n in report if report[n].get("group", "receive") == "receive" and
+             os.path.exists(os.path.join(vdir, f"libzpq_{n}.so"))]
     if "default" not in names:
         raise RuntimeError("the default variant library is missing: run python -m "
                            "block_quantized_communication_amd.build --variants")
@@ -587,6 +593,159 @@ def receive_shapes_study(np, torch, settle_s=0.1):
             "timing": f"per-launch time of {LAUNCHES} back-to-back launches between one HIP event "
                       "pair, buffer sets rotated; the libraries alternate in runs of 5 groups, twice; "
                       "median of the 10 groups", "peak_GBps": HBM_PEAK_GBS}
+
+
+def store_policy_study(np, torch, settle_s=0.1):
+    """The cache-policy bits of streamed loads and stores on this GPU, and of
+    the qgZ quantizer's code stores (bit 0 sc0, bit 1 nt, bit 4 sc1).
+    (1) Read, write and copy streams of 1 GiB and 64 MiB through buffer
+    loads and stores with each of the 8 values (the copy's loads keep nt),
+    one and two 16-byte tiles per lane (bench_patterns.hip).  (2) The qgZ
+    quantizer's bare access pattern with its code stores as non-temporal
+    global stores or as buffer stores with each value.  (3) The quantizer
+    itself: the default build (sc0 sc1 nt) against the QGZ_STORE_VARIANTS
+    builds in block_quantized_communication_amd/variants/, outputs compared
+    byte for byte, writing one output buffer and rotating over enough output
+    buffers (>= 768 MiB) that none stays in the 256 MB last-level cache
+    between two uses.  (2) and (3) on the 2^28 bf16 (L=8, N=4, B=128) and
+    1.06G fp16 (L=8, N=48, B=64) workloads, inputs rotating over two copies."""
+    import ctypes
+    path = os.path.join(ROOT, "libbench_patterns.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libbench_patterns.so is missing: run __graft_entry__.build()")
+    vdir = os.path.join(ROOT, "block_quantized_communication_amd", "variants")
+    rpath = os.path.join(vdir, "resources.json")
+    if not os.path.exists(rpath):
+        raise RuntimeError("no variant libraries: run python -m "
+                           "block_quantized_communication_amd.build --variants")
+    with open(rpath) as f:
+        report = json.load(f)
+    names = ["default"] + [n for n in report if report[n].get("group") == "qgz_store"]
+    missing = [n for n in names if not os.path.exists(os.path.join(vdir, f"libzpq_{n}.so"))]
+    if missing or len(names) < 2:
+        raise RuntimeError(f"variant libraries missing ({missing or 'qgz_store'}): run python -m "
+                           "block_quantized_communication_amd.build --variants")
+    P = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P.pat_stream_pol.argtypes = [i32, i32, i32, vp, vp, i64, vp, vp]
+    P.pat_reorder_quant_i4_pol.argtypes = [i32, vp, i64, i32, i32, i32, vp, vp, vp]
+    P.pat_policy_bits.argtypes = [i32]
+    libs = {}
+    for n in names:
+        lib = ctypes.CDLL(os.path.join(vdir, f"libzpq_{n}.so"))
+        lib.zpq_qgz_reorder_quant_i4.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp]
+        libs[n] = lib
+    bits = [P.pat_policy_bits(i) for i in range(8)]
+
+    def pol_name(b):
+        return " ".join(x for x, m in (("sc0", 1), ("nt", 2), ("sc1", 16)) if b & m) or "none"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed ({rc})")
+    # (1) streams
+    streams = []
+    for size in (1 << 30, 64 << 20):
+        # Sources are only read, destinations only written: a line a store
+        # leaves in the last-level cache is never read back.
+        nbuf = max(1, -(-ROTATE_BYTES // size))
+        srcs = [torch.full((size,), 1, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        dsts = [torch.empty(size, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        for kind, kname in ((0, "read"), (1, "write"), (2, "copy")):
+            for tpl in (1, 2):
+                for pol in range(8):
+                    def mk(j, kind=kind, tpl=tpl, pol=pol):
+                        a = (kind, pol, tpl, srcs[j].data_ptr(), dsts[j].data_ptr(), size,
+                             sink.data_ptr(), st)
+                        return lambda: check(P.pat_stream_pol(*a), "stream")
+                    us = float(np.median(launch_groups_us(
+                        torch, [mk(j) for j in range(nbuf)], 7, settle_s)))
+                    moved = size * (2 if kind == 2 else 1)
+                    streams.append({"stream": kname, "bytes": size, "tiles_per_lane": tpl,
+                                    "policy": pol_name(bits[pol]), "us": round(us, 2),
+                                    "frac_of_peak": round(moved / us / 1e3 / HBM_PEAK_GBS, 4)})
+                print(f"[store-policy] {kname} {size >> 20} MiB, {tpl} tile(s) per lane: "
+                      + ", ".join(f"{r['policy']} {r['frac_of_peak']:.3f}" for r in streams[-8:]),
+                      file=sys.stderr, flush=True)
+        del srcs, dsts
+        torch.cuda.empty_cache()
+    # (2) and (3) on the two qgZ quantizer workloads
+    W = [("2^28 bf16, L=8, N=4, B=128", 1 << 28, 8, 4, 128, 2, 6),
+         ("1.06G fp16, L=8, N=48, B=64", 1056964608, 8, 48, 64, 1, 3)]
+    pattern_rows, kernel_rows = [], []
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12)
+    for label, n, L, N, B, dt, nout in W:
+        nbytes = n * 2 + n // 2 + n // B * 4
+        xs = [(torch.randn(n, device=dev, generator=gen) * 1e-2).to(
+            torch.bfloat16 if dt == 2 else torch.float16) for _ in range(2)]
+        outs = [(torch.empty(n // 2, dtype=torch.uint8, device=dev),
+                 torch.empty(n // B, dtype=torch.float32, device=dev)) for _ in range(nout)]
+        # (2) pattern: -1 = non-temporal global stores, 0..7 = policies
+        times = {p: [] for p in range(-1, 8)}
+        for rep in range(2):
+            for p in (range(-1, 8) if rep == 0 else reversed(range(-1, 8))):
+                def mkp(i, p=p):
+                    x, (cd, sc) = xs[i % 2], outs[i % nout]
+                    a = (p, x.data_ptr(), n, L, N, B, cd.data_ptr(), sc.data_ptr(), st)
+                    return lambda: check(P.pat_reorder_quant_i4_pol(*a), "pattern")
+                times[p] += launch_groups_us(torch, [mkp(i) for i in range(2 * nout)], 5, settle_s)
+        for p in range(-1, 8):
+            us = float(np.median(times[p]))
+            pattern_rows.append({"workload": label, "code_stores": "global nt" if p < 0 else
+                                 "buffer " + pol_name(bits[p]), "us": round(us, 2),
+                                 "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        print(f"[store-policy] pattern {label}: " + ", ".join(
+            f"{r['code_stores']} {r['us']}" for r in pattern_rows[-9:]), file=sys.stderr, flush=True)
+        # (3) the kernel, per build: one output buffer, then rotating outputs
+        ref = None
+        same = {}
+        for nm in names:
+            cd, sc = outs[0]
+            cd.zero_()
+            sc.zero_()
+            check(libs[nm].zpq_qgz_reorder_quant_i4(xs[0].data_ptr(), dt, n, L, N, B, cd.data_ptr(),
+                                                    sc.data_ptr(), st), nm)
+            torch.cuda.synchronize()
+            got = (cd.clone(), sc.clone())
+            ref = got if ref is None else ref
+            same[nm] = all(torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+                           for a, b in zip(ref, got))
+            del got
+        for rot in (False, True):
+            times = {nm: [] for nm in names}
+            for rep in range(2):
+                for nm in (names if rep == 0 else names[::-1]):
+                    def mkk(i, nm=nm):
+                        x, (cd, sc) = xs[i % 2], outs[i % nout if rot else 0]
+                        a = (x.data_ptr(), dt, n, L, N, B, cd.data_ptr(), sc.data_ptr(), st)
+                        f = libs[nm].zpq_qgz_reorder_quant_i4
+                        return lambda: check(f(*a), nm)
+                    times[nm] += launch_groups_us(torch, [mkk(i) for i in range(2 * nout)], 5,
+                                                  settle_s)
+            for nm in names:
+                us = float(np.median(times[nm]))
+                kernel_rows.append({"workload": label, "build": nm,
+                                    "defines": report.get(nm, {}).get("defines", []),
+                                    "outputs": f"{nout} rotating" if rot else "one",
+                                    "us": round(us, 2),
+                                    "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                                    "identical_to_default": same[nm]})
+            print(f"[store-policy] kernel {label}, {'rotating' if rot else 'one'} output(s): " +
+                  ", ".join(f"{r['build']} {r['us']}" for r in kernel_rows[-len(names):]),
+                  file=sys.stderr, flush=True)
+        del xs, outs
+        torch.cuda.empty_cache()
+    return {"study": "store-policy", "streams": streams, "qgz_pattern": pattern_rows,
+            "qgz_kernel": kernel_rows,
+            "timing": f"per-launch time of {LAUNCHES} back-to-back launches between one HIP event "
+                      "pair over rotating buffers; streams: median of 7 groups; pattern and kernel "
+                      "variants alternate in runs of 5 groups, twice, median of the 10 groups",
+            "peak_GBps": HBM_PEAK_GBS}
 
 
 def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):

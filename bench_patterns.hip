@@ -81,6 +81,44 @@ __global__ __launch_bounds__(kThreads) void k_copy(const u32x4* __restrict__ src
     }
 }
 
+// The same streams with every cache-policy value of the buffer loads and
+// stores (AUX: bit 0 sc0, bit 1 nt, bit 4 sc1; the copy's loads keep nt) and
+// TPL 16-byte tiles per lane; `bytes` a multiple of 4096 * TPL, below 4 GiB.
+template <int AUX, int TPL>
+__global__ __launch_bounds__(kThreads) void k_write_pol(void* dst, uint32_t bytes) {
+    const auto r = rsrc(dst, bytes);
+    const uint32_t base = blockIdx.x * (TPL * kThreads) + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+        const uint32_t off = (base + u * kThreads) * 16;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{off, 1u, 2u, 3u}, r, off, 0, AUX);
+    }
+}
+template <int AUX, int TPL>
+__global__ __launch_bounds__(kThreads) void k_read_pol(const void* src, uint32_t bytes,
+                                                       uint32_t* __restrict__ sink) {
+    const auto r = rsrc(src, bytes);
+    const uint32_t base = blockIdx.x * (TPL * kThreads) + threadIdx.x;
+    uint32_t x = 0;
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+        x ^= fold(__builtin_amdgcn_raw_buffer_load_b128(r, (base + u * kThreads) * 16, 0, AUX));
+    if (x == 0x9E3779B9u) sink[threadIdx.x] = x;
+}
+template <int AUX, int TPL>
+__global__ __launch_bounds__(kThreads) void k_copy_pol(const void* src, void* dst, uint32_t bytes) {
+    const auto rs = rsrc(src, bytes), rd = rsrc(dst, bytes);
+    const uint32_t base = blockIdx.x * (TPL * kThreads) + threadIdx.x;
+    u32x4 v[TPL];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + u * kThreads) * 16, 0, 2);
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, (base + u * kThreads) * 16, 0, AUX);
+}
+constexpr int kPolicies[8] = {0, 1, 2, 3, 16, 17, 18, 19};
+
 // ---------------------------------------------------------------------------
 // qwZ quantize (fp16 in, block 256): per lane and tile one 16-byte load (8
 // elements), one 8-byte code store, one scale store per 32 lanes; two tiles
@@ -126,6 +164,9 @@ __global__ __launch_bounds__(kThreads) void k_pat_dequant_i8(const u32x2* __rest
 // lane, one 16-byte load and one 4-byte code store per lane and tile (a
 // buffer store with cache policy sc0 sc1 nt through a descriptor based at the
 // workgroup's codes, as libzpq), one scale store per block.
+// CPOL: the code stores' cache-policy bits (19 as libzpq), or -1 for
+// non-temporal global stores.
+template <int CPOL>
 __global__ __launch_bounds__(kThreads) void k_pat_reorder_quant_i4(
     const u32x4* __restrict__ g, int64_t S, int32_t L, int32_t N, uint32_t wgs_per_slice,
     int32_t block, uint32_t* __restrict__ codes, uint32_t* __restrict__ scales) {
@@ -147,7 +188,10 @@ __global__ __launch_bounds__(kThreads) void k_pat_reorder_quant_i4(
         const int64_t f = f0 + u * (kThreads * 8) + threadIdx.x * 8;
         if (f < S) {
             const int64_t e = dst0 + f;
-            __builtin_amdgcn_raw_buffer_store_b32(fold(v[u]), rc, (uint32_t)(f - f0) / 2, 0, 19);
+            if constexpr (CPOL >= 0)
+                __builtin_amdgcn_raw_buffer_store_b32(fold(v[u]), rc, (uint32_t)(f - f0) / 2, 0, CPOL);
+            else
+                stnt(fold(v[u]), codes + e / 8);
             if ((threadIdx.x & (lanes_per_block - 1)) == 0) scales[e / block] = v[u].x;
         }
     }
@@ -474,11 +518,66 @@ int pat_reorder_quant_i4(const void* g, int64_t n, int32_t L, int32_t N, int32_t
                          void* codes, void* scales, void* st) {
     const int64_t S = n / ((int64_t)L * N);
     const unsigned wps = grid_for(S, 2 * kThreads * 8);
-    hipLaunchKernelGGL(k_pat_reorder_quant_i4, dim3(wps * (unsigned)(L * N)), dim3(kThreads), 0,
+    hipLaunchKernelGGL(k_pat_reorder_quant_i4<19>, dim3(wps * (unsigned)(L * N)), dim3(kThreads), 0,
                        (hipStream_t)st, (const u32x4*)g, S, L, N, wps, block, (uint32_t*)codes,
                        (uint32_t*)scales);
     return hipGetLastError();
 }
+
+// The same with the code stores' cache policy `pol` (0 .. 7: the bits of
+// kPolicies[pol]) or non-temporal global stores (pol = -1).
+int pat_reorder_quant_i4_pol(int32_t pol, const void* g, int64_t n, int32_t L, int32_t N,
+                             int32_t block, void* codes, void* scales, void* st) {
+    typedef void (*kf)(const u32x4*, int64_t, int32_t, int32_t, uint32_t, int32_t, uint32_t*,
+                       uint32_t*);
+    static const kf tab[9] = {k_pat_reorder_quant_i4<-1>, k_pat_reorder_quant_i4<0>,
+                              k_pat_reorder_quant_i4<1>, k_pat_reorder_quant_i4<2>,
+                              k_pat_reorder_quant_i4<3>, k_pat_reorder_quant_i4<16>,
+                              k_pat_reorder_quant_i4<17>, k_pat_reorder_quant_i4<18>,
+                              k_pat_reorder_quant_i4<19>};
+    if (pol < -1 || pol > 7) return (int)hipErrorInvalidValue;
+    const int64_t S = n / ((int64_t)L * N);
+    const unsigned wps = grid_for(S, 2 * kThreads * 8);
+    hipLaunchKernelGGL(tab[pol + 1], dim3(wps * (unsigned)(L * N)), dim3(kThreads), 0,
+                       (hipStream_t)st, (const u32x4*)g, S, L, N, wps, block, (uint32_t*)codes,
+                       (uint32_t*)scales);
+    return hipGetLastError();
+}
+
+// Policy streams: kind 0 read, 1 write, 2 copy; pol 0 .. 7 (kPolicies); tpl 1 or 2.
+int pat_stream_pol(int32_t kind, int32_t pol, int32_t tpl, const void* src, void* dst,
+                   int64_t bytes, void* sink, void* st) {
+#define ZPQ_POL_ROW(T)                                                                          \
+    {k_read_pol<0, T>, k_read_pol<1, T>, k_read_pol<2, T>, k_read_pol<3, T>, k_read_pol<16, T>,  \
+     k_read_pol<17, T>, k_read_pol<18, T>, k_read_pol<19, T>}
+    typedef void (*rf)(const void*, uint32_t, uint32_t*);
+    typedef void (*wf)(void*, uint32_t);
+    typedef void (*cf)(const void*, void*, uint32_t);
+    static const rf rd[2][8] = {ZPQ_POL_ROW(1), ZPQ_POL_ROW(2)};
+#undef ZPQ_POL_ROW
+    static const wf wr[2][8] = {
+        {k_write_pol<0, 1>, k_write_pol<1, 1>, k_write_pol<2, 1>, k_write_pol<3, 1>,
+         k_write_pol<16, 1>, k_write_pol<17, 1>, k_write_pol<18, 1>, k_write_pol<19, 1>},
+        {k_write_pol<0, 2>, k_write_pol<1, 2>, k_write_pol<2, 2>, k_write_pol<3, 2>,
+         k_write_pol<16, 2>, k_write_pol<17, 2>, k_write_pol<18, 2>, k_write_pol<19, 2>}};
+    static const cf cp[2][8] = {
+        {k_copy_pol<0, 1>, k_copy_pol<1, 1>, k_copy_pol<2, 1>, k_copy_pol<3, 1>,
+         k_copy_pol<16, 1>, k_copy_pol<17, 1>, k_copy_pol<18, 1>, k_copy_pol<19, 1>},
+        {k_copy_pol<0, 2>, k_copy_pol<1, 2>, k_copy_pol<2, 2>, k_copy_pol<3, 2>,
+         k_copy_pol<16, 2>, k_copy_pol<17, 2>, k_copy_pol<18, 2>, k_copy_pol<19, 2>}};
+    if (kind < 0 || kind > 2 || pol < 0 || pol > 7 || (tpl != 1 && tpl != 2) || bytes <= 0 ||
+        bytes >= (1LL << 32) || bytes % (16LL * kThreads * tpl) != 0)
+        return (int)hipErrorInvalidValue;
+    const dim3 grid((unsigned)(bytes / (16LL * kThreads * tpl)));
+    const hipStream_t s = (hipStream_t)st;
+    const uint32_t b = (uint32_t)bytes;
+    if (kind == 0) hipLaunchKernelGGL(rd[tpl - 1][pol], grid, dim3(kThreads), 0, s, src, b, (uint32_t*)sink);
+    else if (kind == 1) hipLaunchKernelGGL(wr[tpl - 1][pol], grid, dim3(kThreads), 0, s, dst, b);
+    else hipLaunchKernelGGL(cp[tpl - 1][pol], grid, dim3(kThreads), 0, s, src, dst, b);
+    return hipGetLastError();
+}
+
+int pat_policy_bits(int32_t pol) { return (pol >= 0 && pol < 8) ? kPolicies[pol] : -1; }
 
 // K sources x c elements; I4 output (out_codes, out_scales) when out_vals is
 // NULL, else 16-bit values.  epl / pf: the launch shape libzpq picks.  parts:

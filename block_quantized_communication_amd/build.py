@@ -3,10 +3,12 @@
   python -m block_quantized_communication_amd.build [-v] [--save-temps]
   python -m block_quantized_communication_amd.build --variants
 
---variants builds the receive-kernel launch-shape variants that
-bench.py --study receive-shapes compares (RECEIVE_VARIANTS: one build-time
-override each) into variants/, with the compiler's register, LDS and
-occupancy report for every receive kernel in variants/resources.json.
+--variants builds, into variants/, the receive-kernel launch-shape variants
+that bench.py --study receive-shapes compares (RECEIVE_VARIANTS) and the
+qgZ-quantizer code-store cache policies that bench.py --study store-policy
+compares (QGZ_STORE_VARIANTS), one build-time override each, with the
+compiler's register, LDS and occupancy report for the kernels concerned in
+variants/resources.json.
 
 Flags: -O3 for gfx950 only; packed-FP32 instructions disabled; no fast-math
 (IEEE division, denormals kept); -fPIC shared library with a C ABI.
@@ -66,6 +68,13 @@ RECEIVE_VARIANTS = {
     "fl_always_narrow": ["-DZPQ_REDUCE_NARROW_WAVES=1048576"],
     "wg3": ["-DZPQ_REDUCE_WG3=1"],
 }
+# The qgZ quantizer's code stores (default: buffer stores with sc0 sc1 nt).
+QGZ_STORE_VARIANTS = {
+    "qgz_global_nt": ["-DZPQ_CPOL_QGZ=-1"],      # non-temporal global stores
+    "qgz_nt": ["-DZPQ_CPOL_QGZ=2"],
+    "qgz_sc1": ["-DZPQ_CPOL_QGZ=16"],
+    "qgz_sc0_sc1": ["-DZPQ_CPOL_QGZ=17"],
+}
 VARIANTS_DIR = os.path.join(HERE, "variants")
 
 
@@ -93,18 +102,20 @@ def _resources(stderr, only="k_dequant_reduce"):
 
 
 def build_variants(names=None, jobs=8, verbose=False):
-    """Build the RECEIVE_VARIANTS libraries (all, or `names`) into
-    variants/libzpq_<name>.so, `jobs` compilers at a time; write the
-    compiler's resource report of each variant's receive kernels to
-    variants/resources.json.  Returns the paths."""
+    """Build the RECEIVE_VARIANTS and QGZ_STORE_VARIANTS libraries (all, or
+    `names`) into variants/libzpq_<name>.so, `jobs` compilers at a time; write
+    the compiler's resource report of each variant's receive kernels (or qgZ
+    quantizer kernels) to variants/resources.json, with the variant's group
+    ("receive" or "qgz_store").  Returns the paths."""
     import concurrent.futures
     import json
     os.makedirs(VARIANTS_DIR, exist_ok=True)
-    names = list(RECEIVE_VARIANTS) if names is None else list(names)
+    table = {**RECEIVE_VARIANTS, **QGZ_STORE_VARIANTS}
+    names = list(table) if names is None else list(names)
 
     def one(name):
         out = os.path.join(VARIANTS_DIR, f"libzpq_{name}.so")
-        cmd = ["hipcc", *HIPCC_FLAGS, *RECEIVE_VARIANTS[name], "-Rpass-analysis=kernel-resource-usage",
+        cmd = ["hipcc", *HIPCC_FLAGS, *table[name], "-Rpass-analysis=kernel-resource-usage",
                f"-I{INCLUDE}", SRC, "-o", out + ".tmp"]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -112,12 +123,14 @@ def build_variants(names=None, jobs=8, verbose=False):
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed for variant {name} ({res.returncode}):\n{res.stderr[-4000:]}")
         os.replace(out + ".tmp", out)
-        return name, out, _resources(res.stderr)
+        only = "k_dequant_reduce" if name in RECEIVE_VARIANTS else "k_reorder_quant_i4"
+        return name, out, _resources(res.stderr, only)
 
     report, paths = {}, []
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         for name, out, res in ex.map(one, names):
-            report[name] = {"defines": RECEIVE_VARIANTS[name], "kernels": res}
+            report[name] = {"defines": table[name], "kernels": res,
+                            "group": "receive" if name in RECEIVE_VARIANTS else "qgz_store"}
             paths.append(out)
     rpath = os.path.join(VARIANTS_DIR, "resources.json")
     old = {}

@@ -233,3 +233,10 @@ def test_variant_build_reads_the_compiler_resource_report():
                                 "waves_per_simd": 8, "lds_bytes": 0}
     assert all(v for v in hip_build.RECEIVE_VARIANTS.values() if v) and \
         hip_build.RECEIVE_VARIANTS["default"] == []
+    # the qgZ store-policy variants: their own kernels' report, names apart
+    # from the receive variants, each overriding only the code-store policy
+    assert list(hip_build._resources(text, "k_quant_i8")) == [
+        "_ZN12_GLOBAL__N_110k_quant_i8ILi1ELi256ELi8ELi2EEEvPKvlPaPfj"]
+    assert not set(hip_build.QGZ_STORE_VARIANTS) & set(hip_build.RECEIVE_VARIANTS)
+    assert all(len(v) == 1 and v[0].startswith("-DZPQ_CPOL_QGZ=")
+               for v in hip_build.QGZ_STORE_VARIANTS.values())
