@@ -1027,16 +1027,19 @@ __device__ __forceinline__ void finish_tile(const float (&acc)[EPL], int64_t e,
         const float s = a >= 0x1p-118f ? div_f64(a, 1.0 / 7.0) : a / 7.0f;
         uint32_t packed[EPL / 8];
         {
-            // Codes from one binary32 product.  With a normal scale s, r
+            // Codes from the exact product x * r.  With a normal scale s, r
             // within one ulp of 1/s (the hardware reciprocal refined by one
-            // Newton step) and |x| <= a <= 7.0000009 s, t = fl32(x * r) lies
-            // within 1.4 * 2^-20 of fl32(x / s): unless t is within 2^-19 of
-            // a half-integer, both round to the same integer, so rint_even(t)
-            // is the code.  A lane holding a value that close (or a scale
-            // below 2^-126) takes the binary64 route for all its codes.
-            // Checked on the CPU, with both floats next to 1/s, for every
-            // value within 16 ulp of every rounding boundary of
-            // quantizer-produced scales in every binade.
+            // Newton step) and |x| <= a <= 7.0000009 s, x * r lies within
+            // 2^-20.1 of x / s, and fl32(x / s) within 2^-22 of x / s: unless
+            // x * r is within 2^-19 of a half-integer, rint_even(x * r) and
+            // rint_even(fl32(x / s)) are the same integer.  One fused
+            // multiply-add with 1.5 * 2^23 rounds the product to that integer
+            // (in the low bits of y), a second gives the residual x * r - q.
+            // A lane holding a value that close (or a scale below 2^-126)
+            // takes the binary64 route for all its codes.  Checked on the
+            // CPU, with both floats next to 1/s, for every value within 16
+            // ulp of every rounding boundary of quantizer-produced scales in
+            // every binade.
             const float r0 = __builtin_amdgcn_rcpf(s);
             const float r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
             bool near = !(s >= 0x1p-126f);
@@ -1045,9 +1048,8 @@ __device__ __forceinline__ void finish_tile(const float (&acc)[EPL], int64_t e,
                 uint32_t q[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float t = acc[8 * k + j] * r;
-                    const float y = t + 12582912.0f;          // 1.5 * 2^23: rint_even(t) in the low bits
-                    const float d = t - (y - 12582912.0f);
+                    const float y = __builtin_fmaf(acc[8 * k + j], r, 12582912.0f);
+                    const float d = __builtin_fmaf(acc[8 * k + j], r, -(y - 12582912.0f));
                     near |= fabsf(d) > 0.5f - 0x1p-19f;
                     q[j] = __float_as_uint(y);
                 }

@@ -25,13 +25,14 @@
  *   fastcodes Q T   the same scales and values for the hop-1 requantization's
  *               faster code route: with a normal scale, r either of the two
  *               floats next to 1/s (the kernel refines the hardware
- *               reciprocal to one of them) and t = fl32(x * r), the code is
- *               rint_even(t) unless t lies within 2^-19 of a half-integer
- *               (then, and for scales below 2^-126, the binary64 route
- *               above): every value that takes the fast route, with either
- *               r, gets the definition's code.  Each (value, r) pair is a
- *               case.  Output adds "near K", the pairs sent to the binary64
- *               route.
+ *               reciprocal to one of them), the code is y = rint_even(x * r)
+ *               of the exact product (one fused multiply-add with 1.5 * 2^23)
+ *               unless the residual fl32(x * r - y) (a second fused
+ *               multiply-add) exceeds 0.5 - 2^-19 in magnitude (then, and
+ *               for scales below 2^-126, the binary64 route above): every
+ *               value that takes the fast route, with either r, gets the
+ *               definition's code.  Each (value, r) pair is a case.  Output
+ *               adds "near K", the pairs sent to the binary64 route.
  *   mean T      divisors d = 1..65536, all powers of two 2^-40..2^40 and
  *               200000 random floats in [2^-20, 2^40]; for each, sums next to
  *               binary32 rounding boundaries of the quotient (16 ulp either
@@ -73,11 +74,13 @@ static float k_code(float x, float s, int q) {
     if (!(s >= 0x1p-126f)) t = fminf(fmaxf(t, -(float)q), (float)q);
     return rintf(t);
 }
-/* the hop-1 requantization's faster route: t = fl32(x * RN32(1/s)) is within
- * 2^-19 of fl32(x / s) when s is normal and |x| <= 7.0000009 s (the absmax
- * element included), so rint_even(t) is the code unless t is that close to a
- * half-integer.  PLANT_NARROW_MARGIN shrinks the margin to 2^-30 (a plausible
- * mistake) so that the test can show the checker catching it. */
+/* the hop-1 requantization's faster route: the exact product x * r, r next
+ * to 1/s, is within 7.0000009 * 2^-23 of x / s when s is normal and |x| <=
+ * 7.0000009 s (the absmax element included), and fl32(x / s) within 2^-22 of
+ * x / s, so rint_even of the product is the code unless the product lies
+ * within 2^-19 of a half-integer.  PLANT_NARROW_MARGIN shrinks the margin to
+ * 2^-30 (a plausible mistake) so that the test can show the checker catching
+ * it. */
 #ifdef PLANT_NARROW_MARGIN
 #define FAST_MARGIN (0.5f - 0x1p-30f)
 #else
@@ -85,9 +88,8 @@ static float k_code(float x, float s, int q) {
 #endif
 static float k_code_fast(float x, float s, float r, int q, int* exact_route) {
     if (!(s >= 0x1p-126f)) { *exact_route = 1; return k_code(x, s, q); }
-    const float t = x * r;
-    const float y = (t + 12582912.0f) - 12582912.0f;   /* rint_even(t), |t| < 2^22 */
-    const float d = t - y;
+    const float y = fmaf(x, r, 12582912.0f) - 12582912.0f;   /* rint_even(x * r), |x * r| < 2^22 */
+    const float d = fmaf(x, r, -y);                           /* x * r - y, rounded once */
     if (fabsf(d) > FAST_MARGIN) { *exact_route = 1; return k_code(x, s, q); }
     *exact_route = 0;
     return y;
