@@ -160,6 +160,7 @@ def main():
         return
     if args.study == "receive-shapes":
         print(json.dumps(receive_shapes_study(np, torch)), flush=True)
+        return
     if args.study == "store-policy":
         print(json.dumps(store_policy_study(np, torch)), flush=True)
         return
@@ -558,8 +559,8 @@ def receive_shapes_study(np, torch, settle_s=0.1):
             torch.cuda.synchronize()
             outs[n] = [t.clone() for t in sets[0][2]]
         times = {n: [] for n in names}
-        for rep in range(2):                       # all libraries in turn, then in reverse
-            for n in (names if rep == 0 else names[::-1]):
+        for rep in range(6):                       # all libraries in turn, then in reverse
+            for n in (names if rep % 2 == 0 else names[::-1]):
                 times[n] += launch_groups_us(torch, [caller(libs[n], x, K, c, B, fl, div)
                                                      for x in sets], 5, settle_s)
         ref = outs["default"]
@@ -591,8 +592,8 @@ def receive_shapes_study(np, torch, settle_s=0.1):
         torch.cuda.empty_cache()
     return {"study": "receive-shapes", "rows": rows, "hop1_source_sweep": ksweep,
             "timing": f"per-launch time of {LAUNCHES} back-to-back launches between one HIP event "
-                      "pair, buffer sets rotated; the libraries alternate in runs of 5 groups, twice; "
-                      "median of the 10 groups", "peak_GBps": HBM_PEAK_GBS}
+                      "pair, buffer sets rotated; the libraries alternate in runs of 5 groups, 6 times "
+                      "(forward, then backward); median of the 30 groups", "peak_GBps": HBM_PEAK_GBS}
 
 
 def store_policy_study(np, torch, settle_s=0.1):

@@ -172,6 +172,30 @@ def test_bench_measures_one_gpu_only():
     assert "one GPU" in r.stderr
 
 
+def test_bench_modes_end_after_their_own_output():
+    """Each alternative mode of bench.py (a study, --per-config, --patterns,
+    ...) prints its one JSON line and returns: none falls through into the
+    throughput benchmark, whose line would follow its own."""
+    import ast
+    with open(os.path.join(ROOT, "bench.py")) as f:
+        tree = ast.parse(f.read())
+    main = next(n for n in tree.body if isinstance(n, ast.FunctionDef) and n.name == "main")
+    studies = set()
+    for node in main.body:
+        if not isinstance(node, ast.If) or node.orelse:
+            continue
+        test = ast.unparse(node.test)
+        if not test.startswith("args."):
+            continue
+        m = re.fullmatch(r"args\.study == '([a-z-]+)'", test)
+        if m:
+            studies.add(m.group(1))
+        if re.fullmatch(r"args\.(study == '[a-z-]+'|per_config|patterns|valu_rates)", test):
+            assert isinstance(node.body[-1], ast.Return), test
+    choices = next(k for k in ast.walk(tree) if isinstance(k, ast.keyword) and k.arg == "choices")
+    assert studies == {c.value for c in choices.value.elts}
+
+
 def test_binding_refuses_host_tensors():
     """The binding passes raw pointers: tensors not on a GPU are refused in
     Python, before the library sees them."""
