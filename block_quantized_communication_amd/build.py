@@ -56,11 +56,13 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
 RECEIVE_VARIANTS = {
     "default": [],
     "i4_pf1": ["-DZPQ_REDUCE_PF_I4=1"],
+    "i4_pf3": ["-DZPQ_REDUCE_PF_I4=3"],
     "i4_pf4": ["-DZPQ_REDUCE_PF_I4=4"],
     "i4_epl16": ["-DZPQ_REDUCE_EPL_I4=16"],
     "i4_epl16_pf4": ["-DZPQ_REDUCE_EPL_I4=16", "-DZPQ_REDUCE_PF_I4=4"],
     "fl_narrow_pf2": ["-DZPQ_REDUCE_PF_FL_NARROW=2"],
     "fl_narrow_pf8": ["-DZPQ_REDUCE_PF_FL_NARROW=8"],
+    "fl_wide_pf3": ["-DZPQ_REDUCE_PF_FL=3"],
     "fl_wide_pf4": ["-DZPQ_REDUCE_PF_FL=4"],
     "fl_wide_epl32": ["-DZPQ_REDUCE_EPL_FL=32"],
     "fl_wide_xcd": ["-DZPQ_XCD_REDUCE=1"],
