@@ -120,13 +120,15 @@ def parse():
                     help="measure the vector ALU's issue rate per instruction kind and per "
                          "per-element sequence of the hop-receive loop (register-only kernels "
                          "from bench_patterns.hip)")
-    ap.add_argument("--study", choices=["hop-count", "blocking", "receive-shapes", "store-policy"],
+    ap.add_argument("--study", choices=["hop-count", "blocking", "receive-shapes", "store-policy",
+                                        "timeline"],
                     default=None,
                     help="run a study instead of the throughput benchmark: hop-count and "
                          "blocking (quantization error), receive-shapes (launch shapes of the "
                          "receive kernel; needs the variant libraries), store-policy (cache-policy "
                          "bits of streams and of the qgZ quantizer's code stores; needs the "
-                         "variant libraries)")
+                         "variant libraries), timeline (every wave's start and end in the receive "
+                         "launches and their bare patterns; needs the variant libraries)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 1 GiB with torch (a plain copy kernel of known "
                          "size, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -163,6 +165,9 @@ def main():
         return
     if args.study == "store-policy":
         print(json.dumps(store_policy_study(np, torch)), flush=True)
+        return
+    if args.study == "timeline":
+        print(json.dumps(timeline_study(np, torch)), flush=True)
         return
     if args.per_config:
         print(json.dumps(per_config(np, torch, zpq, synth)), flush=True)
@@ -747,6 +752,157 @@ def store_policy_study(np, torch, settle_s=0.1):
                       "pair over rotating buffers; streams: median of 7 groups; pattern and kernel "
                       "variants alternate in runs of 5 groups, twice, median of the 10 groups",
             "peak_GBps": HBM_PEAK_GBS}
+
+
+def timeline_summary(np, start_us, end_us, nbytes):
+    """Occupancy and progress of one launch from its waves' start and end
+    times (us from the first start).  The byte rate over time assumes each
+    wave moves its share of the launch's bytes evenly over its lifetime (an
+    estimate: a wave issues its loads ahead of its arithmetic)."""
+    s, e = np.asarray(start_us, np.float64), np.asarray(end_us, np.float64)
+    span, dt = float(e.max()), 0.05
+    grid = np.arange(0.0, span + dt, dt)
+    conc = np.zeros(len(grid))
+    rate = np.zeros(len(grid))
+    per = nbytes / len(s)
+    i0 = (s / dt).astype(np.int64)
+    i1 = (e / dt).astype(np.int64)
+    for a, b, ls in zip(i0, i1, np.maximum(e - s, dt)):
+        conc[a:b + 1] += 1
+        rate[a:b + 1] += per / ls                  # bytes per us
+    cum = np.cumsum(rate) * dt
+    t90 = float(grid[min(len(grid) - 1, int(np.searchsorted(cum, 0.9 * nbytes)))])
+    mid = rate[(grid > 0.2 * span) & (grid < 0.7 * span)]
+    life = e - s
+    return {"span_us": round(span, 2), "peak_waves": int(conc.max()),
+            "mean_waves_over_peak": round(float(conc.mean() / conc.max()), 3),
+            "wave_life_us_p10_p50_p90": [round(float(x), 2) for x in np.percentile(life, [10, 50, 90])],
+            "last_wave_start_us": round(float(s.max()), 2),
+            "last_10pct_of_bytes_us": round(span - t90, 2),
+            "mid_launch_rate_frac_of_peak": round(float(np.median(mid)) / 1e3 / HBM_PEAK_GBS, 3),
+            "avg_rate_frac_of_peak": round(nbytes / span / 1e3 / HBM_PEAK_GBS, 3)}
+
+
+def timeline_study(np, torch, settle_s=0.2):
+    """Every wave's start and end (the 100 MHz constant clock) in the four
+    receive launches and in their bare access patterns: how full the GPU is
+    over a launch, how long a wave lives, how fast bytes move mid-launch and
+    how long the last tenth of them takes.  The kernel runs from the
+    recording builds of block_quantized_communication_amd/variants/
+    (timeline_w8 for the INT4 kernel, timeline for the float ones; the study
+    reports their registers beside the shipped kernel's and their time with
+    recording off beside libzpq's); the pattern is bench_patterns.hip's with
+    parts 7.  Each launch is recorded alone and as the last of 20
+    back-to-back launches."""
+    import ctypes
+    vdir = os.path.join(ROOT, "block_quantized_communication_amd", "variants")
+    rpath = os.path.join(vdir, "resources.json")
+    ppath = os.path.join(ROOT, "libbench_patterns.so")
+    if not os.path.exists(ppath):
+        raise RuntimeError("libbench_patterns.so is missing: run __graft_entry__.build()")
+    if not os.path.exists(rpath):
+        raise RuntimeError("no variant libraries: run python -m "
+                           "block_quantized_communication_amd.build --variants")
+    with open(rpath) as f:
+        report = json.load(f)
+    for n in ("default", "timeline", "timeline_w8"):
+        if n not in report or not os.path.exists(os.path.join(vdir, f"libzpq_{n}.so")):
+            raise RuntimeError(f"variant library {n} missing: run python -m "
+                               "block_quantized_communication_amd.build --variants")
+    vp, i32, i64, f32, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint32
+    libs = {}
+    for n in ("default", "timeline", "timeline_w8"):
+        lib = ctypes.CDLL(os.path.join(vdir, f"libzpq_{n}.so"))
+        lib.zpq_qgz_dequant_reduce_requant_i4.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32,
+                                                          f32, vp]
+        if n != "default":
+            lib.zpq_timeline_set.argtypes = [vp, u32]
+        libs[n] = lib
+    P = ctypes.CDLL(ppath)
+    P.pat_receive.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32, vp]
+    P.pat_timeline_set.argtypes = [vp, u32]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(13)
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed ({rc})")
+    W = [("c3 hop 1: 8 x 2^25 -> INT4, B=128", 8, 1 << 25, 128, 0, 1.0),
+         ("c4 hop 2: 16 x 2^24 -> bf16 average, B=128", 16, 1 << 24, 128, 2, 16.0),
+         ("c5 hop 1: 8 x 132M -> INT4, B=64", 8, 132120576, 64, 0, 1.0),
+         ("c5 hop 2: 48 x 2.75M -> fp16 average, B=64", 48, 2752512, 64, 1, 384.0)]
+    rows = []
+    for label, K, c, B, fl, div in W:
+        nbytes = K * (c // 2 + c // B * 4) + (c * 2 if fl else c // 2 + c // B * 4)
+        sets = []
+        for _ in range(n_sets(nbytes)):
+            codes = torch.randint(0, 256, (K * c // 2,), dtype=torch.uint8, device=dev, generator=gen)
+            scales = torch.rand(K * c // B, device=dev, generator=gen) * 1e-3 + 1e-6
+            out = ((torch.empty(c, dtype=torch.int16, device=dev),) if fl else
+                   (torch.empty(c // 2, dtype=torch.uint8, device=dev),
+                    torch.empty(c // B, dtype=torch.float32, device=dev)))
+            sets.append((codes, scales, out))
+        epl, pf, nt, frag = receive_launch([], K, c, B, fl, cus)
+        probe = "timeline" if fl else "timeline_w8"
+        waves = -(-c // (64 * epl))
+
+        def kern(lib, x):
+            codes, scales, out = x
+            if fl:
+                a = (codes.data_ptr(), scales.data_ptr(), K, c, B, None, None, out[0].data_ptr(),
+                     fl, div, st)
+            else:
+                a = (codes.data_ptr(), scales.data_ptr(), K, c, B, out[0].data_ptr(),
+                     out[1].data_ptr(), None, 0, 1.0, st)
+            f = lib.zpq_qgz_dequant_reduce_requant_i4
+            return lambda: check(f(*a), "receive")
+
+        def pat(x):
+            codes, scales, out = x
+            a = (codes.data_ptr(), scales.data_ptr(), K, c, B, None if fl else out[0].data_ptr(),
+                 None if fl else out[1].data_ptr(), out[0].data_ptr() if fl else None, epl, pf, 7, st)
+            return lambda: check(P.pat_receive(*a), "pattern")
+        res_of = lambda n: next((r for k, r in report[n]["kernels"].items() if frag in k), {})
+        row = {"workload": label, "waves": waves, "elements_per_lane": epl, "sources_in_flight": pf,
+               "bytes": nbytes, "probe_build": probe,
+               "registers_shipped": res_of("default"), "registers_probe": res_of(probe)}
+        times = {"default": [], probe: []}
+        for rep in range(4):
+            for n in (("default", probe) if rep % 2 == 0 else (probe, "default")):
+                times[n] += launch_groups_us(torch, [kern(libs[n], x) for x in sets], 5, settle_s)
+        row["libzpq_us"] = round(float(np.median(times["default"])), 2)
+        row["probe_us_recording_off"] = round(float(np.median(times[probe])), 2)
+        buf = torch.zeros(2 * waves, dtype=torch.int64, device=dev)
+        for what, setter, fns in (("kernel", libs[probe].zpq_timeline_set,
+                                   [kern(libs[probe], x) for x in sets]),
+                                  ("pattern", P.pat_timeline_set, [pat(x) for x in sets])):
+            check(setter(None, 0), "timeline reset")
+            launch_groups_us(torch, fns, 1, settle_s)          # warm, recording off
+            for mode in ("alone", "last_of_20"):
+                buf.zero_()
+                torch.cuda.synchronize()
+                check(setter(ctypes.c_void_p(buf.data_ptr()), waves), "timeline set")
+                for i in range(1 if mode == "alone" else LAUNCHES):
+                    fns[i % len(fns)]()
+                torch.cuda.synchronize()
+                check(setter(None, 0), "timeline reset")
+                t = buf.view(waves, 2).cpu().numpy().astype(np.float64)
+                ok = (t[:, 0] > 0) & (t[:, 1] >= t[:, 0])
+                if not ok.all():
+                    raise RuntimeError(f"{label} {what}: {int((~ok).sum())} waves not recorded")
+                t0 = t[:, 0].min()
+                row[f"{what}_{mode}"] = timeline_summary(np, (t[:, 0] - t0) / 100.0,
+                                                         (t[:, 1] - t0) / 100.0, nbytes)
+            print(f"[timeline] {label} {what}: " + json.dumps(row[f"{what}_last_of_20"]),
+                  file=sys.stderr, flush=True)
+        rows.append(row)
+        del sets, buf
+        torch.cuda.empty_cache()
+    return {"study": "timeline", "rows": rows, "clock_MHz": 100, "peak_GBps": HBM_PEAK_GBS}
 
 
 def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):

@@ -22,6 +22,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Wave timeline of the receive pattern (pat_receive with parts bit 2): lane 0
+// of each wave stores the 100 MHz constant clock at its start and end.
+__device__ uint64_t* pat_tl_buf = nullptr;
+__device__ uint32_t pat_tl_waves = 0;
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -235,15 +240,24 @@ __device__ __forceinline__ void mix(uint32_t (&acc)[EPL / 8], const Src<EPL>& d)
     for (int i = 0; i < EPL / 8; ++i) acc[i] ^= d.w[i] ^ d.s;
 }
 
+__device__ __forceinline__ void pat_mark(int which) {
+    if (pat_tl_buf != nullptr && (threadIdx.x & 63) == 0) {
+        const uint32_t w = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+        if (w < pat_tl_waves)
+            __builtin_nontemporal_store(__builtin_amdgcn_s_memrealtime(), pat_tl_buf + 2 * w + which);
+    }
+}
+
 // SC: the per-source scale loads; ST: the output stores (both true for the
-// pattern proper; the others decompose its time).
-template <int EPL, int PF, bool I4, bool SC, bool ST>
+// pattern proper; the others decompose its time); TL: record the wave timeline.
+template <int EPL, int PF, bool I4, bool SC, bool ST, bool TL = false>
 __global__ __launch_bounds__(kThreads) void k_pat_receive(
     const uint8_t* __restrict__ in_codes, const uint32_t* __restrict__ in_scales, int32_t K,
     int64_t c, int32_t block, uint8_t* __restrict__ out_codes, uint32_t* __restrict__ out_scales,
     uint16_t* __restrict__ out_vals) {
     constexpr int V = I4 ? 1 : EPL / 8;          // 16-byte output vectors per lane (float output)
     __shared__ u32x4 stage[V >= 2 ? kThreads / 64 : 1][V >= 2 ? V * 64 : 1];
+    if constexpr (TL) pat_mark(0);
     const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * EPL;
     if (e >= c) return;
     const int64_t cs = c / 2, ss = c / block;
@@ -315,6 +329,7 @@ __global__ __launch_bounds__(kThreads) void k_pat_receive(
             for (int k = 0; k < V; ++k) stnt(o[k], dst + k);
         }
     }
+    if constexpr (TL) pat_mark(1);
 }
 
 // ---------------------------------------------------------------------------
@@ -468,6 +483,8 @@ int launch_pat_receive(unsigned g, unsigned nt, hipStream_t s, const uint8_t* ic
                                ic, is, K, c, block, oc, os, ov); break;
     case 0: hipLaunchKernelGGL((k_pat_receive<EPL, PF, I4, false, false>), dim3(g), dim3(nt), 0, s,
                                ic, is, K, c, block, oc, os, ov); break;
+    case 7: hipLaunchKernelGGL((k_pat_receive<EPL, PF, I4, true, true, true>), dim3(g), dim3(nt), 0,
+                               s, ic, is, K, c, block, oc, os, ov); break;
     default: return (int)hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -581,7 +598,8 @@ int pat_policy_bits(int32_t pol) { return (pol >= 0 && pol < 8) ? kPolicies[pol]
 
 // K sources x c elements; I4 output (out_codes, out_scales) when out_vals is
 // NULL, else 16-bit values.  epl / pf: the launch shape libzpq picks.  parts:
-// bit 0 the scale loads, bit 1 the stores (3: the kernel's whole pattern).
+// bit 0 the scale loads, bit 1 the stores (3: the kernel's whole pattern);
+// 7: the whole pattern, recording the wave timeline (pat_timeline_set).
 int pat_receive(const void* in_codes, const void* in_scales, int32_t K, int64_t c, int32_t block,
                 void* out_codes, void* out_scales, void* out_vals, int32_t epl, int32_t pf,
                 int32_t parts, void* st) {
@@ -600,6 +618,14 @@ int pat_receive(const void* in_codes, const void* in_scales, int32_t K, int64_t 
     if (out_vals && epl == 8 && pf == 4)
         return launch_pat_receive<8, 4, false>(g, nt, s, ic, is, K, c, block, oc, os, ov, parts);
     return (int)hipErrorInvalidValue;
+}
+
+// Where pat_receive with parts 7 records wave times: 2 words per wave for
+// the first `waves` waves (NULL: nowhere).
+int pat_timeline_set(void* buf, uint32_t waves) {
+    if (hipMemcpyToSymbol(HIP_SYMBOL(pat_tl_buf), &buf, sizeof(buf)) != hipSuccess) return 1;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(pat_tl_waves), &waves, sizeof(waves)) != hipSuccess) return 2;
+    return 0;
 }
 
 // VALU issue-rate kernel `kind` (0 .. pat_valu_kinds() - 1) on `wgs`

@@ -4,9 +4,10 @@
   python -m block_quantized_communication_amd.build --variants
 
 --variants builds, into variants/, the receive-kernel launch-shape variants
-that bench.py --study receive-shapes compares (RECEIVE_VARIANTS) and the
+that bench.py --study receive-shapes compares (RECEIVE_VARIANTS), the
 qgZ-quantizer code-store cache policies that bench.py --study store-policy
-compares (QGZ_STORE_VARIANTS), one build-time override each, with the
+compares (QGZ_STORE_VARIANTS) and the wave-timeline recording builds of
+bench.py --study timeline (TIMELINE_VARIANTS), one build-time override each, with the
 compiler's register, LDS and occupancy report for the kernels concerned in
 variants/resources.json.
 
@@ -70,6 +71,13 @@ RECEIVE_VARIANTS = {
     "fl_always_narrow": ["-DZPQ_REDUCE_NARROW_WAVES=1048576"],
     "wg3": ["-DZPQ_REDUCE_WG3=1"],
 }
+# Wave-timeline recording builds of the receive kernel (bench.py --study
+# timeline): timeline_w8 holds the occupancy target at 8 waves per SIMD, where
+# the recording code would otherwise change the INT4 kernel's registers.
+TIMELINE_VARIANTS = {
+    "timeline": ["-DZPQ_TIMELINE=1"],
+    "timeline_w8": ["-DZPQ_TIMELINE=1", "-DZPQ_TIMELINE_WAVES=8"],
+}
 # The qgZ quantizer's code stores (default: buffer stores with sc0 sc1 nt).
 QGZ_STORE_VARIANTS = {
     "qgz_global_nt": ["-DZPQ_CPOL_QGZ=-1"],      # non-temporal global stores
@@ -112,7 +120,7 @@ def build_variants(names=None, jobs=8, verbose=False):
     import concurrent.futures
     import json
     os.makedirs(VARIANTS_DIR, exist_ok=True)
-    table = {**RECEIVE_VARIANTS, **QGZ_STORE_VARIANTS}
+    table = {**RECEIVE_VARIANTS, **QGZ_STORE_VARIANTS, **TIMELINE_VARIANTS}
     names = list(table) if names is None else list(names)
 
     def one(name):
@@ -125,14 +133,15 @@ def build_variants(names=None, jobs=8, verbose=False):
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed for variant {name} ({res.returncode}):\n{res.stderr[-4000:]}")
         os.replace(out + ".tmp", out)
-        only = "k_dequant_reduce" if name in RECEIVE_VARIANTS else "k_reorder_quant_i4"
+        only = "k_reorder_quant_i4" if name in QGZ_STORE_VARIANTS else "k_dequant_reduce"
         return name, out, _resources(res.stderr, only)
 
     report, paths = {}, []
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         for name, out, res in ex.map(one, names):
             report[name] = {"defines": table[name], "kernels": res,
-                            "group": "receive" if name in RECEIVE_VARIANTS else "qgz_store"}
+                            "group": ("receive" if name in RECEIVE_VARIANTS else
+                                      "qgz_store" if name in QGZ_STORE_VARIANTS else "timeline")}
             paths.append(out)
     rpath = os.path.join(VARIANTS_DIR, "resources.json")
     old = {}

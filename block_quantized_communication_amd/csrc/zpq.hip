@@ -86,6 +86,17 @@
 #ifndef ZPQ_REDUCE_WG3
 #define ZPQ_REDUCE_WG3 0           // receive: 3-wave workgroups where they spread waves more evenly
 #endif
+// Measurement builds only (never the shipped library): the receive kernel
+// records each wave's start and end time (the 100 MHz constant clock) into a
+// buffer set by zpq_timeline_set; ZPQ_TIMELINE_WAVES > 0 also fixes its
+// occupancy target, so that the recording code does not change the register
+// allocation the shipped kernel has.
+#ifndef ZPQ_TIMELINE
+#define ZPQ_TIMELINE 0
+#endif
+#ifndef ZPQ_TIMELINE_WAVES
+#define ZPQ_TIMELINE_WAVES 0
+#endif
 // Persistent grids: workgroups per compute unit (0 = one workgroup per
 // virtual block, no loop).
 #ifndef ZPQ_PERSIST_QUANT
@@ -147,6 +158,11 @@
 #endif
 #ifndef ZPQ_NTS_REDUCE
 #define ZPQ_NTS_REDUCE 1
+#endif
+
+#if ZPQ_TIMELINE
+__device__ uint64_t* zpq_tl_buf = nullptr;     // 2 words per wave: start, end
+__device__ uint32_t zpq_tl_waves = 0;
 #endif
 
 namespace {
@@ -989,8 +1005,27 @@ __device__ __forceinline__ void reduce_tile(
 template <int OUT, int EPL>
 struct OutVectors { static constexpr int v = OUT < 0 ? 0 : EPL * (OUT == ZPQ_F32 ? 4 : 2) / 16; };
 
+#if ZPQ_TIMELINE && ZPQ_TIMELINE_WAVES > 0
+#define ZPQ_REDUCE_ATTR __attribute__((amdgpu_waves_per_eu(ZPQ_TIMELINE_WAVES, ZPQ_TIMELINE_WAVES)))
+#else
+#define ZPQ_REDUCE_ATTR
+#endif
+
+// Wave timeline (measurement builds): lane 0 of each wave stores the clock.
+__device__ __forceinline__ void timeline_mark(int which) {
+#if ZPQ_TIMELINE
+    if (zpq_tl_buf != nullptr && (threadIdx.x & 63) == 0) {
+        const uint32_t w = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+        if (w < zpq_tl_waves)
+            __builtin_nontemporal_store(__builtin_amdgcn_s_memrealtime(), zpq_tl_buf + 2 * w + which);
+    }
+#else
+    (void)which;
+#endif
+}
+
 template <int BLOCK, int EPL, int OUT /* -1: INT4, else a zpq_dtype */, int PF>
-__global__ __launch_bounds__(kThreads) void k_dequant_reduce(
+__global__ __launch_bounds__(kThreads) ZPQ_REDUCE_ATTR void k_dequant_reduce(
     const uint8_t* __restrict__ in_codes, const float* __restrict__ in_scales, int32_t K,
     int64_t c, uint8_t* __restrict__ out_codes, float* __restrict__ out_scales,
     void* __restrict__ out_vals, Avg avg, uint32_t nvb) {
@@ -999,6 +1034,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
     u32x4* const slice = &stage[V >= 2 ? threadIdx.x / 64 : 0][0];
     // kThreads threads per workgroup, or kThreads - 64 where a build with
     // ZPQ_REDUCE_WG3 picks 3-wave workgroups (reduce_threads).
+    timeline_mark(0);
     for (uint32_t k = blockIdx.x; k < nvb; k += gridDim.x) {
     const uint32_t vb = tile_of<ZPQ_XCD_REDUCE>(k, nvb);
         const int64_t e = ((int64_t)vb * blockDim.x + threadIdx.x) * EPL;
@@ -1006,6 +1042,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_reduce(
             reduce_tile<BLOCK, EPL, OUT, PF>(in_codes, in_scales, K, c, out_codes, out_scales,
                                              out_vals, avg, e, slice);
     }
+    timeline_mark(1);
 }
 
 // The epilogue of a tile: requantize the sums to INT4 codes and block
@@ -1570,5 +1607,15 @@ const char* zpq_status_str(zpq_status s) {
 }
 
 int32_t zpq_abi_version(void) { return ZPQ_ABI_VERSION; }
+
+#if ZPQ_TIMELINE
+// Measurement builds: where the receive kernel records wave times (2 words
+// per wave, for the first `waves` waves of each launch; NULL stops it).
+int32_t zpq_timeline_set(void* buf, uint32_t waves) {
+    if (hipMemcpyToSymbol(HIP_SYMBOL(zpq_tl_buf), &buf, sizeof(buf)) != hipSuccess) return 1;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(zpq_tl_waves), &waves, sizeof(waves)) != hipSuccess) return 2;
+    return 0;
+}
+#endif
 
 }  // extern "C"

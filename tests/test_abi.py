@@ -262,5 +262,8 @@ def test_variant_build_reads_the_compiler_resource_report():
     assert list(hip_build._resources(text, "k_quant_i8")) == [
         "_ZN12_GLOBAL__N_110k_quant_i8ILi1ELi256ELi8ELi2EEEvPKvlPaPfj"]
     assert not set(hip_build.QGZ_STORE_VARIANTS) & set(hip_build.RECEIVE_VARIANTS)
+    assert not set(hip_build.TIMELINE_VARIANTS) & (set(hip_build.RECEIVE_VARIANTS) |
+                                                   set(hip_build.QGZ_STORE_VARIANTS))
+    assert all("-DZPQ_TIMELINE=1" in v for v in hip_build.TIMELINE_VARIANTS.values())
     assert all(len(v) == 1 and v[0].startswith("-DZPQ_CPOL_QGZ=")
                for v in hip_build.QGZ_STORE_VARIANTS.values())
