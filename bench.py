@@ -789,11 +789,13 @@ def timeline_study(np, torch, settle_s=0.2):
     over a launch, how long a wave lives, how fast bytes move mid-launch and
     how long the last tenth of them takes.  The kernel runs from the
     recording builds of block_quantized_communication_amd/variants/
-    (timeline_w8 for the INT4 kernel, timeline for the float ones; the study
+    (timeline_w7 for the INT4 kernel, timeline for the float ones; the study
     reports their registers beside the shipped kernel's and their time with
     recording off beside libzpq's); the pattern is bench_patterns.hip's with
     parts 7.  Each launch is recorded alone and as the last of 20
-    back-to-back launches."""
+    back-to-back launches.  First, bench_patterns.hip's residency probes: the
+    most waves of one kernel a SIMD holds at once, by the kernel's scalar
+    register count (64 VGPRs each)."""
     import ctypes
     vdir = os.path.join(ROOT, "block_quantized_communication_amd", "variants")
     rpath = os.path.join(vdir, "resources.json")
@@ -805,13 +807,13 @@ def timeline_study(np, torch, settle_s=0.2):
                            "block_quantized_communication_amd.build --variants")
     with open(rpath) as f:
         report = json.load(f)
-    for n in ("default", "timeline", "timeline_w8"):
+    for n in ("default", "timeline", "timeline_w7"):
         if n not in report or not os.path.exists(os.path.join(vdir, f"libzpq_{n}.so")):
             raise RuntimeError(f"variant library {n} missing: run python -m "
                                "block_quantized_communication_amd.build --variants")
     vp, i32, i64, f32, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint32
     libs = {}
-    for n in ("default", "timeline", "timeline_w8"):
+    for n in ("default", "timeline", "timeline_w7"):
         lib = ctypes.CDLL(os.path.join(vdir, f"libzpq_{n}.so"))
         lib.zpq_qgz_dequant_reduce_requant_i4.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32,
                                                           f32, vp]
@@ -821,6 +823,7 @@ def timeline_study(np, torch, settle_s=0.2):
     P = ctypes.CDLL(ppath)
     P.pat_receive.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32, vp]
     P.pat_timeline_set.argtypes = [vp, u32]
+    P.pat_residency.argtypes = [i32, vp, u32, i32, vp]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -831,6 +834,26 @@ def timeline_study(np, torch, settle_s=0.2):
     def check(rc, what):
         if rc != 0:
             raise RuntimeError(f"{what} failed ({rc})")
+    # residency by scalar registers: 16 waves per SIMD of each probe
+    residency = []
+    rw = 16 * 4 * cus
+    rbuf = torch.zeros(2 * rw, dtype=torch.int64, device=dev)
+    for i in range(P.pat_residency_count()):
+        rbuf.zero_()
+        torch.cuda.synchronize()
+        check(P.pat_residency(i, rbuf.data_ptr(), rw, 5, st), "residency probe")
+        torch.cuda.synchronize()
+        t = rbuf.view(rw, 2).cpu().numpy().astype(np.float64)
+        if not ((t[:, 0] > 0) & (t[:, 1] >= t[:, 0])).all():
+            raise RuntimeError("residency probe: waves not recorded")
+        s0, e0 = t[:, 0] - t[:, 0].min(), t[:, 1] - t[:, 0].min()
+        ev = np.concatenate([np.stack([s0, np.ones(rw)], 1), np.stack([e0, -np.ones(rw)], 1)])
+        ev = ev[np.lexsort((ev[:, 1], ev[:, 0]))]            # ends before starts at equal times
+        peak = int(np.cumsum(ev[:, 1]).max())
+        residency.append({"sgprs_reported": P.pat_residency_sgprs(i), "vgprs": 64,
+                          "peak_waves": peak, "waves_per_simd": round(peak / (4 * cus), 2)})
+        print(f"[timeline] residency {residency[-1]}", file=sys.stderr, flush=True)
+    del rbuf
     W = [("c3 hop 1: 8 x 2^25 -> INT4, B=128", 8, 1 << 25, 128, 0, 1.0),
          ("c4 hop 2: 16 x 2^24 -> bf16 average, B=128", 16, 1 << 24, 128, 2, 16.0),
          ("c5 hop 1: 8 x 132M -> INT4, B=64", 8, 132120576, 64, 0, 1.0),
@@ -847,7 +870,7 @@ def timeline_study(np, torch, settle_s=0.2):
                     torch.empty(c // B, dtype=torch.float32, device=dev)))
             sets.append((codes, scales, out))
         epl, pf, nt, frag = receive_launch([], K, c, B, fl, cus)
-        probe = "timeline" if fl else "timeline_w8"
+        probe = "timeline" if fl else "timeline_w7"
         waves = -(-c // (64 * epl))
 
         def kern(lib, x):
@@ -902,7 +925,8 @@ def timeline_study(np, torch, settle_s=0.2):
         rows.append(row)
         del sets, buf
         torch.cuda.empty_cache()
-    return {"study": "timeline", "rows": rows, "clock_MHz": 100, "peak_GBps": HBM_PEAK_GBS}
+    return {"study": "timeline", "residency_by_sgprs": residency, "rows": rows, "clock_MHz": 100,
+            "peak_GBps": HBM_PEAK_GBS}
 
 
 def hop_count_study(np, torch, zpq, synth, S=1 << 20, B=128, seed=40):

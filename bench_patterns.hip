@@ -490,6 +490,35 @@ int launch_pat_receive(unsigned g, unsigned nt, hipStream_t s, const uint8_t* ic
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Residency: how many waves of a kernel a SIMD holds at once, by the kernel's
+// scalar register count.  Each probe kernel reserves 64 VGPRs and the SGPRs up
+// to a given one (empty asm clobbers: the compiler then reports that many plus
+// 7 more in use), then sleeps a fixed number of times; lane 0 of each wave
+// records its start and end in the timeline buffer (2 words per wave).
+#define ZPQ_RES_BODY(CLOB)                                                        \
+    const uint32_t w = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;          \
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();                          \
+    asm volatile("" ::: CLOB, "v63");                                            \
+    for (int i = 0; i < iters; ++i) __builtin_amdgcn_s_sleep(64);                  \
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();                          \
+    if ((threadIdx.x & 63) == 0 && w < n) { ts[2 * w] = t0; ts[2 * w + 1] = t1; }
+__global__ __launch_bounds__(kThreads) void k_res76(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s69") }
+__global__ __launch_bounds__(kThreads) void k_res78(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s71") }
+__global__ __launch_bounds__(kThreads) void k_res80(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s73") }
+__global__ __launch_bounds__(kThreads) void k_res81(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s74") }
+__global__ __launch_bounds__(kThreads) void k_res82(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s75") }
+__global__ __launch_bounds__(kThreads) void k_res96(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s89") }
+__global__ __launch_bounds__(kThreads) void k_res97(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s90") }
+__global__ __launch_bounds__(kThreads) void k_res98(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s91") }
+__global__ __launch_bounds__(kThreads) void k_res104(uint64_t* ts, uint32_t n, int iters) { ZPQ_RES_BODY("s97") }
+#undef ZPQ_RES_BODY
+typedef void (*res_fn)(uint64_t*, uint32_t, int);
+const res_fn kResKernels[] = {k_res76, k_res78, k_res80, k_res81, k_res82, k_res96, k_res97, k_res98, k_res104};
+const int kResSgprs[] = {76, 78, 80, 81, 82, 96, 97, 98, 104};   // as the compiler reports them
+constexpr int kNumRes = sizeof(kResSgprs) / sizeof(kResSgprs[0]);
+
 }  // namespace
 
 extern "C" {
@@ -626,6 +655,19 @@ int pat_timeline_set(void* buf, uint32_t waves) {
     if (hipMemcpyToSymbol(HIP_SYMBOL(pat_tl_buf), &buf, sizeof(buf)) != hipSuccess) return 1;
     if (hipMemcpyToSymbol(HIP_SYMBOL(pat_tl_waves), &waves, sizeof(waves)) != hipSuccess) return 2;
     return 0;
+}
+
+// Residency probe `i` (0 .. pat_residency_count() - 1): `waves` waves (a
+// multiple of 4) in 256-thread workgroups, each sleeping `iters` (1..4096)
+// times 64 x 64 cycles; times into `ts` (2 words per wave).
+int pat_residency_count(void) { return kNumRes; }
+int pat_residency_sgprs(int i) { return (i >= 0 && i < kNumRes) ? kResSgprs[i] : -1; }
+int pat_residency(int i, void* ts, uint32_t waves, int32_t iters, void* st) {
+    if (i < 0 || i >= kNumRes || waves == 0 || waves % 4 != 0 || iters < 1 || iters > 4096)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(kResKernels[i], dim3(waves / 4), dim3(kThreads), 0, (hipStream_t)st,
+                       (uint64_t*)ts, waves, iters);
+    return hipGetLastError();
 }
 
 // VALU issue-rate kernel `kind` (0 .. pat_valu_kinds() - 1) on `wgs`

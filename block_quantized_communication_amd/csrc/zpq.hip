@@ -89,8 +89,8 @@
 // Measurement builds only (never the shipped library): the receive kernel
 // records each wave's start and end time (the 100 MHz constant clock) into a
 // buffer set by zpq_timeline_set; ZPQ_TIMELINE_WAVES > 0 also fixes its
-// occupancy target, so that the recording code does not change the register
-// allocation the shipped kernel has.
+// occupancy target, so that the recording code does not change the number of
+// waves per SIMD the shipped kernel gets.
 #ifndef ZPQ_TIMELINE
 #define ZPQ_TIMELINE 0
 #endif
